@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a printed or
+textbook value, a closed form, an exhaustive enumeration, an exact rational
+computation, an independent library routine, or an invariant that a dropped term,
+a wrong sign, a wrong index or a transposed operand would break."""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ----------------------------------------------------------------------------- formats
+
+def test_e2m1_table_exhaustive():
+    table = {int(c): float(v) for c, v in _golden("e2m1_values.txt")}
+    got = O.e2m1_decode(np.arange(16))
+    for c in range(16):
+        assert got[c] == table[c]
+        assert math.copysign(1.0, got[c]) == math.copysign(1.0, table[c]) or table[c] == 0.0
+    # the value set of the format
+    assert sorted(set(np.abs(got).tolist())) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e8m0_all_codes_closed_form():
+    got = O.e8m0_decode(np.arange(256))
+    for c in range(255):
+        assert Fraction(float(got[c])) == Fraction(2) ** (c - 127)
+    assert np.isnan(got[255])
+
+
+def test_bf16_round_matches_torch_and_ties_to_even():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 20000).astype(np.float32),
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130, 3.39e38, 0.0, -0.0], dtype=np.float32),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(O.bf16_round(x).view(np.uint32), ref.view(np.uint32))
+    # hand ties: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> even (1); 1 + 3*2^-8 -> 1 + 2^-6
+    assert O.bf16_round(np.float32(1 + 2 ** -8)) == 1.0
+    assert O.bf16_round(np.float32(1 + 3 * 2 ** -8)) == np.float32(1 + 2 ** -6)
+
+
+def test_bf16_from_f64_single_rounding():
+    # A float64 just above a bf16 midpoint must round up; rounding through float32 first
+    # would land on the midpoint and round to even (down).
+    x = 1 + 2 ** -8 + 2 ** -40
+    assert O.bf16_from_f64(np.array([x]))[0] == np.float32(1 + 2 ** -7)
+    assert O.bf16_from_f64(np.array([1 + 2 ** -8]))[0] == 1.0
+    assert O.bf16_from_f64(np.array([-1.4621171572600098]))[0] == np.float32(-1.4609375)
+    assert O.bf16_from_f64(np.array([2.0 ** -133]))[0] == np.float32(2.0 ** -133)
+    assert np.isinf(O.bf16_from_f64(np.array([3.5e38]))[0])
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal(5000) * 3
+    # float64 -> bf16 equals float64 -> exact rational rounding by brute force
+    for t in v[:300]:
+        r = float(O.bf16_from_f64(np.array([t]))[0])
+        m, e = math.frexp(t)
+        lo = math.ldexp(math.floor(math.ldexp(t, 8 - e)), e - 8)
+        hi = lo + math.ldexp(1.0, e - 8)
+        assert r in (lo, hi)
+        d_lo, d_hi = abs(Fraction(t) - Fraction(lo)), abs(Fraction(hi) - Fraction(t))
+        assert (r == lo and d_lo <= d_hi) or (r == hi and d_hi <= d_lo)
+
+
+# ----------------------------------------------------------------------------- packing
+
+def test_nibble_order_from_pairnib_packer():
+    # selective_state_update_pairnib.py, pack_pairnib: byte = even | (odd << 4)
+    assert O.pack_nibbles(np.array([[1, 2, 15, 0]])).tolist() == [[0x21, 0x0F]]
+    assert O.pack_nibbles(np.array([[-1, -8, 7, -2]])).tolist() == [[0x8F, 0xE7]]
+
+
+def test_nibble_roundtrip_exhaustive():
+    allbytes = np.arange(256, dtype=np.uint8).reshape(4, 64)
+    assert np.array_equal(O.pack_nibbles(O.unpack_nibbles(allbytes)), allbytes)
+    rng = np.random.default_rng(2)
+    c = rng.integers(0, 16, size=(37, 512))
+    assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(c)), c)
+    s = rng.integers(-8, 8, size=(5, 64))
+    assert np.array_equal(O.sign_extend4(O.unpack_nibbles(O.pack_nibbles(s))), s)
+
+
+# ----------------------------------------------------------------------------- INT4
+
+def test_int4_sym_worked_example():
+    g = np.zeros(128, dtype=np.float32)
+    g[:3] = [0.7, -0.35, 0.1]
+    q, s = O.quantize_int4_sym(g[None, :], 128)
+    s32 = np.float32(np.float16(np.float32(0.7) / np.float32(7)))
+    assert s[0, 0] == np.float16(s32)
+    assert q[0, 0] == 7 and q[0, 1] == round(-0.35 / float(s32)) and q[0, 2] == 1
+    # exact ties of w/s round to the even integer
+    w = np.zeros((1, 128), dtype=np.float32)
+    s0 = np.float32(0.125)
+    w[0, :5] = np.array([7, 2.5, 3.5, -2.5, 0.5], dtype=np.float32) * s0
+    q, s = O.quantize_int4_sym(w, 128)
+    assert s[0, 0] == np.float16(0.125)
+    assert q[0, :5].tolist() == [7, 2, 4, -2, 0]
+
+
+def test_int4_sym_on_grid_exact():
+    rng = np.random.default_rng(3)
+    N, K, G = 16, 512, 128
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    q[:, ::G] = rng.choice([-7, 7], size=(N, K // G))        # every group reaches |q| = 7
+    s = (rng.uniform(1e-3, 1e-1, (N, K // G))).astype(np.float16)
+    w = O.dequant_int4(O.pack_nibbles(q), s, None, G)
+    q2, s2 = O.quantize_int4_sym(w, G)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+
+
+def test_int4_asym_on_grid_exact_and_formula():
+    rng = np.random.default_rng(4)
+    N, K, G = 16, 512, 128
+    q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    q[:, 0::G] = 0
+    q[:, 1::G] = 15                                   # each group spans the full code range
+    z = rng.integers(0, 16, size=(N, K // G)).astype(np.uint8)
+    s = (rng.uniform(1e-3, 1e-1, (N, K // G))).astype(np.float16)
+    w = O.dequant_int4(O.pack_nibbles(q), s, z, G)
+    # w = s (q - z), checked element by element with exact rationals
+    for (n, k) in [(0, 0), (3, 129), (15, 511), (7, 200)]:
+        assert Fraction(float(w[n, k])) == Fraction(float(s[n, k // G])) * (int(q[n, k]) - int(z[n, k // G]))
+    q2, s2, z2 = O.quantize_int4_asym(w, G)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s) and np.array_equal(z2, z)
+
+
+def test_int4_rtn_error_bound_and_zero_group():
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((8, 1024)).astype(np.float32) * np.float32(0.02)
+    w[3, 128:256] = 0.0
+    q, s = O.quantize_int4_sym(w, 128)
+    d = O.dequant_int4(O.pack_nibbles(q), s, None, 128)
+    step = np.repeat(s.astype(np.float32), 128, axis=1)
+    assert np.all(np.abs(d - w) <= step / 2 * (1 + 1e-6) + 1e-12)
+    assert s[3, 1] == 0 and np.all(q[3, 128:256] == 0)
+    assert q.min() >= -8 and q.max() <= 7
+    qa, sa, za = O.quantize_int4_asym(w, 128)
+    da = O.dequant_int4(O.pack_nibbles(qa), sa, za, 128)
+    step = np.repeat(sa.astype(np.float32), 128, axis=1)
+    assert np.all(np.abs(da - w) <= step / 2 * (1 + 1e-3) + 1e-12)
+    assert sa[3, 1] == 0 and za[3, 1] == 0 and np.all(qa[3, 128:256] == 0)
+
+
+# ----------------------------------------------------------------------------- INT8
+
+def test_int8_on_grid_exact_and_bound():
+    rng = np.random.default_rng(6)
+    N, K, G = 8, 1024, 256
+    q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    q[:, ::G] = rng.choice([-127, 127], size=(N, K // G))
+    s = O.bf16_round(rng.uniform(1e-4, 1e-2, (N, K // G)).astype(np.float32))
+    w = O.dequant_int8(q, s, G)
+    q2, s2 = O.quantize_int8(w, G)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    w = rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.015)
+    q, s = O.quantize_int8(w, G)
+    d = O.dequant_int8(q, s, G)
+    assert np.all(np.abs(d - w) <= np.repeat(s, G, axis=1) * 0.5000001 + 1e-12)
+    assert q.min() >= -127
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+def test_mxfp4_element_rounding_ties_and_saturation():
+    v = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 100.0, -0.1, -0.25, -0.3, 5.01, 0.2499])
+    codes = O.e2m1_nearest(v)
+    assert O.e2m1_decode(codes).tolist() == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, 6.0, 0.0, 0.0, -0.5, 6.0, 0.0]
+    assert codes[9] == 0 and codes[10] == 0         # no negative zero
+
+
+def test_mxfp4_scale_rule_closed_form():
+    for amax, e in [(1.0, -2), (0.02, -8), (6.0, 0), (7.99, 0), (8.0, 1), (2.0 ** -130, -127)]:
+        w = np.zeros((1, 32), dtype=np.float32)
+        w[0, 5] = amax
+        _, sc = O.quantize_mxfp4(w)
+        assert int(sc[0, 0]) - 127 == e, (amax, sc)
+    _, sc = O.quantize_mxfp4(np.zeros((1, 32), dtype=np.float32))
+    assert sc[0, 0] == 127
+
+
+def test_mxfp4_on_grid_exact():
+    rng = np.random.default_rng(7)
+    N, K = 8, 256
+    q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    q[q == 8] = 0                                       # no negative zero
+    q[:, ::32] = rng.choice([6, 7, 14, 15], size=(N, K // 32))  # each block reaches |4| or |6|
+    e = rng.integers(100, 140, size=(N, K // 32)).astype(np.uint8)
+    w = O.dequant_mxfp4(O.pack_nibbles(q), e)
+    q2, e2 = O.quantize_mxfp4(w)
+    assert np.array_equal(q2, q) and np.array_equal(e2, e)
+
+
+def test_mxfp4_nearest_is_brute_force_nearest():
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    q, e = O.quantize_mxfp4(w)
+    d = O.dequant_mxfp4(O.pack_nibbles(q), e).astype(np.float64)
+    sc = np.repeat(O.e8m0_decode(e).astype(np.float64), 32, axis=1)
+    grid = np.array(sorted(set(O.e2m1_decode(np.arange(16)).tolist())))
+    for n, k in zip(rng.integers(0, 16, 400), rng.integers(0, 256, 400)):
+        cand = grid * sc[n, k]
+        best = np.min(np.abs(cand - w[n, k]))
+        assert abs(d[n, k] - w[n, k]) == best
+
+
+# ----------------------------------------------------------------------------- codebook
+
+def test_lloyd_max_matches_max_1960_table():
+    c, t = O.lloyd_max_gaussian(16)
+    gold = _golden("lloyd_max_gaussian_16.txt")
+    # one unit in the last printed digit of the table
+    ulp = lambda v: 10.0 ** -len(v.split(".")[1])
+    lv = [(float(v), ulp(v)) for k, _, v in gold if k == "level"]
+    th = [(float(v), ulp(v)) for k, _, v in gold if k == "threshold"]
+    mse_tab = [float(v) for k, _, v in gold if k == "mse"][0]
+    assert all(abs(a - v) <= u for a, (v, u) in zip(c[8:], lv))
+    assert all(abs(a - v) <= u for a, (v, u) in zip(t[7:], th))
+    assert np.array_equal(c[:8], -c[8:][::-1])                   # symmetric
+    from scipy import integrate, stats
+    edges = np.concatenate(([-np.inf], t, [np.inf]))
+    mse = 0.0
+    for i in range(16):
+        a, b = edges[i], edges[i + 1]
+        mass = stats.norm.cdf(b) - stats.norm.cdf(a)
+        mean = integrate.quad(lambda x: x * stats.norm.pdf(x), a, b)[0] / mass
+        assert abs(mean - c[i]) < 1e-9                              # centroid condition
+        mse += integrate.quad(lambda x: (x - c[i]) ** 2 * stats.norm.pdf(x), a, b)[0]
+    assert abs(mse - mse_tab) < 1e-5
+
+
+def test_cb4_requantise_with_norms_and_ties():
+    c = O.lloyd_max_gaussian(16)[0].astype(np.float32)
+    rng = np.random.default_rng(9)
+    N, K = 12, 256
+    idx = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    nrm = O.bf16_round(rng.uniform(0.1, 2.0, N).astype(np.float32))
+    w = O.dequant_cb4(O.pack_nibbles(idx), nrm, c, K)
+    i2, n2 = O.quantize_cb4(w, c, norms=nrm)
+    assert np.array_equal(i2, idx) and np.array_equal(n2, nrm)
+    # decode formula w = c[idx] * norm / sqrt(K) with float32 steps
+    s = np.float32(nrm[3]) / np.float32(math.sqrt(K))
+    assert w[3, 17] == np.float32(c[idx[3, 17]]) * s
+    # a value exactly between two centroids goes to the lower index
+    cc = np.array([-1.0, 1.0] + [5.0] * 14, dtype=np.float32)
+    i3, _ = O.quantize_cb4(np.zeros((1, 4), dtype=np.float32), cc, norms=np.array([1.0], dtype=np.float32))
+    assert i3[0, 0] == 0
+    # a zero row has norm 0 and decodes to zeros
+    i4, n4 = O.quantize_cb4(np.zeros((1, 64), dtype=np.float32), c)
+    assert n4[0] == 0 and np.all(O.dequant_cb4(O.pack_nibbles(i4), n4, c, 64) == 0)
+
+
+def test_cb4_norm_is_rounded_row_norm():
+    rng = np.random.default_rng(10)
+    w = (rng.standard_normal((4, 300)) * 0.02).astype(np.float32)
+    _, n = O.quantize_cb4(w, O.lloyd_max_gaussian()[0])
+    for r in range(4):
+        exact = math.sqrt(math.fsum(float(v) ** 2 for v in w[r]))
+        cands = O.bf16_round(np.array([np.nextafter(np.float32(exact), -np.inf), exact,
+                                       np.nextafter(np.float32(exact), np.inf)], dtype=np.float32))
+        assert n[r] in cands
+        assert abs(n[r] - exact) <= exact * 2 ** -8
+
+
+def test_storage_accounting_about_25_percent():
+    for N, K, approx in [(int(a), int(b), float(c)) for a, b, c in _golden("orbitquant_storage.txt")]:
+        b = O.canonical_bytes("cb4", N, K)
+        ratio = (b["codes"] + b["scales"] + b["aux"]) / (2 * N * K)
+        assert abs(ratio - approx) < 0.001
+    b = O.canonical_bytes("cb4", 3072, 3072)
+    assert b["codes"] + b["scales"] + b["aux"] == 3072 * 3072 // 2 + 2 * 3072 + 64
+
+
+# ----------------------------------------------------------------------------- SwiGLU
+
+def test_swiglu_closed_forms():
+    up_gate = np.array([[2.0, 0.0, 3.0, 1.0, 5.0, -50.0]], dtype=np.float32)  # up=[2,0,3] gate=[1,5,-50]
+    h = O.swiglu_bf16(up_gate)
+    silu1 = 1.0 / (1.0 + math.exp(-1.0))
+    assert h[0, 0] == O.bf16_from_f64(np.array([2 * silu1]))[0] == np.float32(1.4609375)
+    assert h[0, 1] == 0.0
+    assert abs(h[0, 2]) < 1e-18                       # 3 * silu(-50) ~ 3 * -50 e^-50
+    assert O.silu64(np.array([0.0]))[0] == 0.0
+    # order of halves: [up | gate], not [gate | up]
+    # up=1, gate=2: silu(2) = 2/(1+e^-2) = 1.76159.. -> bf16 1.7578125 (swapped halves: 1.4609375)
+    assert O.swiglu_bf16(np.array([[1.0, 2.0]], dtype=np.float32))[0, 0] == np.float32(1.7578125)
+
+
+# ----------------------------------------------------------------------------- linear
+
+def _frac_linear(a, dw, bias):
+    M, K = a.shape
+    N = dw.shape[0]
+    out = [[None] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(a[m, k])) * Fraction(float(dw[n, k]))
+            if bias is not None:
+                acc += Fraction(float(bias[n]))
+            out[m][n] = acc
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["int4_sym", "int4_asym", "mxfp4", "int8", "cb4"])
+def test_linear_brute_force_exact_rationals(fmt):
+    rng = np.random.default_rng(11)
+    M, N, K = 3, 4, 256
+    x = S.to_bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    b = S.to_bf16_values((rng.standard_normal(N) * 0.01).astype(np.float32))
+    if fmt == "int4_sym":
+        canon = O.quantize("int4", w, 128, symmetric=True)
+        f = "int4"
+    elif fmt == "int4_asym":
+        canon = O.quantize("int4", w, 64, symmetric=False)
+        f = "int4"
+    elif fmt == "int8":
+        canon = O.quantize("int8", w, 128)
+        f = "int8"
+    else:
+        canon = O.quantize(fmt, w)
+        f = fmt
+    dw = O.dequant(f, canon, K)
+    y = O.linear_ref(x, dw, b)
+    ex = _frac_linear(x, dw, b)
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(y[m, n]) - ex[m][n]) <= abs(ex[m][n]) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+    # dequantised weights stay close to the master weights (catches a wrong scale or sign)
+    assert np.max(np.abs(dw - w)) < 0.25 * np.max(np.abs(w))
+    # swapping the roles of the operands gives a different, wrongly shaped product
+    assert y.shape == (M, N)
+
+
+def test_output_rows_matches_full_forward():
+    rng = np.random.default_rng(12)
+    wl = S.small("int8_swiglu", N=64, K=512)
+    w = S.weights(wl)
+    x = S.activations(wl, 5)
+    b = S.bias(wl)
+    canon = O.quantize("int8", w, 256)
+    y = O.forward("int8", x, canon, 512, b, swiglu=True)
+    rows = rng.integers(0, 5, 40)
+    cols = rng.integers(0, 64, 40)
+    ys = O.output_rows("int8", x, canon, 512, rows, cols, b, swiglu=True)
+    assert np.allclose(ys, y[rows, cols], rtol=1e-12, atol=1e-15)
+
+
+def test_synthetic_workloads_shapes_and_outliers():
+    wl = S.small("mxfp4_up", N=200, K=512)
+    w = S.weights(wl)
+    assert w.shape == (200, 512)
+    plain = S.weights(dict(wl, outlier_frac=None))
+    changed = w != plain
+    assert int(changed.sum()) == round(0.001 * 200 * 512)
+    assert np.allclose(w[changed], 20 * plain[changed])
+    x = S.activations(S.WORKLOADS["int8_swiglu"], 1, K=64)
+    assert x.shape == (1, 128)
+    assert np.array_equal(O.bf16_round(x), x)
