@@ -1,0 +1,267 @@
+"""Benchmark of the weight-only low-bit linear layer on one MI355X.
+
+One step = one forward of the INT4 decode workload with zero-points (group 128, fp16
+scales, 4-bit zeros): X bf16 [16, 4096] times a packed 4096 x 4096 weight, bf16 out.
+The metric is effective HBM bandwidth: algorithmic bytes (packed weight + scales +
+zero-points + X + Y) per step over the step time.  Each step reads a different copy
+of the packed weight from a pool larger than twice the 256 MB Infinity Cache, so the
+weights come from HBM.  Steps run back to back inside a HIP graph (the launch-bound
+inner loop), timed with HIP events on the stream the kernels run on.
+
+Also reported, on the same line:
+  sweep    the decode workload at M = 1, 4, 8, 16
+  prefill  the 4-bit codebook workload at M = 2048 (3072 x 3072): TFLOP/s and the
+           fraction of the dense bf16 matrix-core peak
+  roofline the dominant kernel against the HBM peak (8 TB/s)
+  cpu_baseline  the CPU oracle (dequantise, then a float64 product) on a bounded
+           sample of the same workload, on the host cores
+
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+POOL_BYTES = 1 << 30           # > 2 x the 256 MB Infinity Cache
+
+
+def alg_bytes(fmt, M, N, K, G, zeros, swiglu=False, bias=False):
+    """Algorithmic bytes of one forward: packed codes + scales (+ zeros) + A + Y (+ bias)."""
+    if fmt == "int8":
+        w = N * K
+    else:
+        w = N * K // 2
+    if fmt in ("int4", "int8"):
+        s = 2 * N * (K // G) + (N * (K // G) // 2 if zeros else 0)
+    elif fmt == "mxfp4":
+        s = N * (K // 32)
+    else:
+        s = 2 * N + 64
+    a = M * (2 * K if swiglu else K) * 2
+    y = M * N * 2
+    return w + s + a + y + (2 * N if bias else 0)
+
+
+def _canonical(fmt, N, K, G, sym, seed):
+    import torch
+
+    import synthetic as S
+    rng = np.random.default_rng(seed)
+    codes, scales, aux = S.random_codes(rng, fmt, N, K, G, symmetric=sym)
+    dev = "cuda"
+    c = torch.from_numpy(codes).to(dev)
+    if fmt == "int4":
+        s = torch.from_numpy(scales).to(dev)
+        a = None if aux is None else torch.from_numpy(aux).to(dev)
+    elif fmt == "mxfp4":
+        s = torch.from_numpy(scales).to(dev)
+        a = None
+    else:
+        s = torch.from_numpy(scales.view(np.int16)).to(dev).view(torch.bfloat16)
+        a = None
+    if fmt == "cb4":
+        # a symmetric 16-level codebook (Lloyd-Max levels of N(0,1) to four digits)
+        half = np.array([0.1284, 0.3881, 0.6568, 0.9424, 1.256, 1.618, 2.069, 2.733], dtype=np.float32)
+        a = np.concatenate([-half[::-1], half]).astype(np.float32)
+    return c, s, a
+
+
+def _pool(Q, fmt, N, K, G, sym, seed, pool_bytes):
+    import torch
+    c, s, a = _canonical(fmt, N, K, G, sym, seed)
+    pw = Q.pack(fmt, N, K, G, c, s, a)
+    per = pw.w.numel() + pw.s.numel() + (0 if pw.aux is None else pw.aux.numel())
+    n = max(1, int(np.ceil(pool_bytes / per)))
+    pool = [pw]
+    for _ in range(n - 1):
+        pool.append(Q.PackedWeight(pw.fmt, pw.N, pw.K, pw.group, pw.has_zeros, pw.w.clone(), pw.s.clone(),
+                                   None if pw.aux is None else pw.aux.clone()))
+    torch.cuda.synchronize()
+    return pool
+
+
+def time_forward(Q, pool, x, act, steps, warmup, use_graph=True):
+    """Average time (ms) of one forward over `steps` forwards, each on the next pool copy."""
+    import torch
+    pw0 = pool[0]
+    M = x.shape[0]
+    out = torch.empty((M, pw0.N), dtype=torch.bfloat16, device=x.device)
+    wsb = Q.workspace_bytes(pw0.fmt, M, pw0.N, pw0.K, pw0.group, act)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
+
+    def run(i):
+        Q.linear(x, pool[i % len(pool)], act=act, out=out, workspace=ws)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(steps):
+                    run(i)
+        torch.cuda.synchronize()
+        g.replay()                     # warm replay
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        del g
+    else:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            run(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+    return ms, out
+
+
+def cpu_baseline(wl_name, M, seconds=10.0):
+    """The oracle as it stands (dequantise, then the float64 product) on host cores."""
+    import oracle as O
+    import synthetic as S
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wl = S.WORKLOADS[wl_name]
+    N, K, G = wl["N"], wl["K"], wl["group"]
+    w = S.weights(wl)
+    canon = O.quantize("int4", w, G, symmetric=wl["symmetric"])
+    x = S.activations(wl, M)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        O.forward("int4", x, canon, K)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / n
+    b = alg_bytes("int4", M, N, K, G, not wl["symmetric"])
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full forwards (dequantise + float64 product) of the {N}x{K} INT4 weight at M={M}, "
+                      f"{dt * 1e3:.1f} ms each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time every workload shape")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_weight_only_offline_amd as Q
+    import synthetic as S
+    torch.cuda.set_device(0)
+    use_graph = not args.no_graph
+
+    wl = S.WORKLOADS["int4_asym_decode"]
+    N, K, G = wl["N"], wl["K"], wl["group"]
+    pool = _pool(Q, "int4", N, K, G, False, 2, POOL_BYTES)
+    n_copies = len(pool)
+    xs = S.activations(wl, 16)
+    sweep = {}
+    main_ms = None
+    for M in (1, 4, 8, 16):
+        x = torch.from_numpy(xs[:M]).cuda().to(torch.bfloat16)
+        st = args.steps if M == 16 else max(50, args.steps // 2)
+        ms, _ = time_forward(Q, pool, x, None, st, args.warmup, use_graph)
+        b = alg_bytes("int4", M, N, K, G, True)
+        sweep[str(M)] = {"us": round(ms * 1e3, 3), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)}
+        if M == 16:
+            main_ms = ms
+    del pool
+    torch.cuda.empty_cache()
+    b16 = alg_bytes("int4", 16, N, K, G, True)
+    value = b16 / (main_ms * 1e-3) / 1e9
+
+    # prefill: 4-bit codebook, 3072 x 3072, M = 2048
+    wl5 = S.WORKLOADS["cb4_prefill"]
+    pool5 = _pool(Q, "cb4", wl5["N"], wl5["K"], 0, True, 5, 256 << 20)
+    x5 = torch.from_numpy(S.activations(wl5, 2048)).cuda().to(torch.bfloat16)
+    ms5, _ = time_forward(Q, pool5, x5, None, max(20, args.steps // 4), max(3, args.warmup // 4), use_graph)
+    fl = 2.0 * 2048 * wl5["N"] * wl5["K"]
+    tflops = fl / (ms5 * 1e-3) / 1e12
+    prefill = {"workload": "cb4 Lloyd-Max codebook 3072x3072, M=2048, bf16", "us": round(ms5 * 1e3, 2),
+               "TFLOP/s": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    del pool5
+    torch.cuda.empty_cache()
+
+    others = {}
+    if args.all:
+        for name, M_list in (("mxfp4_up", (1, 16, 64)), ("mxfp4_down", (1, 16, 64)), ("int8_swiglu", (1, 16, 128)),
+                             ("cb4_prefill", (256,))):
+            w_ = S.WORKLOADS[name]
+            fmt = w_["fmt"]
+            pl = _pool(Q, fmt, w_["N"], w_["K"], w_["group"], True, 7, POOL_BYTES)
+            for M in M_list:
+                xa = torch.from_numpy(S.activations(w_, M)).cuda().to(torch.bfloat16)
+                act = "swiglu" if w_.get("swiglu") else None
+                ms, _ = time_forward(Q, pl, xa, act, max(20, args.steps // 4), 5, use_graph)
+                b = alg_bytes(fmt, M, w_["N"], w_["K"], w_["group"], False, bool(act), w_.get("bias_std") is not None)
+                fl = 2.0 * M * w_["N"] * w_["K"]
+                others[f"{name}/M{M}"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                                          "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1)}
+            del pl
+            torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu else cpu_baseline("int4_asym_decode", 16, args.cpu_seconds)
+    rec = {
+        "metric": "W4A16 linear: effective HBM GB/s at M=1-16; TFLOP/s + MFMA util at M=2048",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "int4 asym g128 decode linear, W 4096x4096 (fp16 scales, 4-bit zeros), "
+                               "X bf16 [16,4096], bf16 out", "M": 16, "N": N, "K": K, "group": G,
+                   "weight_pool_copies": n_copies, "hip_graph": use_graph},
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "sweep": sweep,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    if others:
+        rec["others"] = others
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

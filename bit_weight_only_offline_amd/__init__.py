@@ -1,0 +1,225 @@
+"""Python binding of libqlinear.so, the MI355X weight-only low-bit linear layer.
+
+Argument marshalling only: every function checks dtypes and shapes, allocates the
+output with PyTorch on the input's device and passes raw pointers, sizes and the
+current HIP stream to the C ABI declared in include/qlinear.h.  All arithmetic runs
+in the library's HIP kernels.  There is no fallback: if the library is missing or no
+GPU is present, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "QL_INT4", "QL_MXFP4", "QL_INT8", "QL_CB4", "FORMATS", "QLinearError", "lib", "version",
+    "PackedWeight", "packed_bytes", "pack", "unpack", "dequant_tile", "workspace_bytes", "linear",
+]
+
+QL_INT4, QL_MXFP4, QL_INT8, QL_CB4 = 0, 1, 2, 3
+FORMATS = {"int4": QL_INT4, "mxfp4": QL_MXFP4, "int8": QL_INT8, "cb4": QL_CB4}
+_ACT = {None: 0, "none": 0, "swiglu": 1}
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlinear.so")
+_lib = None
+
+
+class QLinearError(RuntimeError):
+    """A non-zero ql_status from the library."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqlinear.so from the package directory (built by build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise QLinearError(f"{_LIB_PATH} is missing: build it with python -m bit_weight_only_offline_amd.build")
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, sz, vp, ci = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+        L.qlinear_version.restype = ci
+        L.qlinear_error_string.restype = ctypes.c_char_p
+        L.qlinear_error_string.argtypes = [ci]
+        L.qlinear_packed_bytes.restype = ci
+        L.qlinear_packed_bytes.argtypes = [ci, i64, i64, ci, ci, ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                           ctypes.POINTER(sz)]
+        L.qlinear_pack.restype = ci
+        L.qlinear_pack.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.qlinear_unpack.restype = ci
+        L.qlinear_unpack.argtypes = [ci, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.qlinear_dequant_tile.restype = ci
+        L.qlinear_dequant_tile.argtypes = [ci, i64, i64, ci, ci, vp, vp, vp, i64, i64, i64, i64, ci, vp, vp]
+        L.qlinear_workspace_bytes.restype = ci
+        L.qlinear_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ci, ctypes.POINTER(sz)]
+        L.qlinear_forward.restype = ci
+        L.qlinear_forward.argtypes = [vp, i64, i64, i64, vp, vp, vp, ci, ci, ci, vp, ci, vp, ci, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return int(lib().qlinear_version())
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().qlinear_error_string(status).decode()
+        raise QLinearError(f"{what}: {msg} (status {status})")
+
+
+def _fmt(f) -> int:
+    return FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(device) -> torch.device:
+    d = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if d.type != "cuda":
+        raise QLinearError("the library runs on a HIP device only")
+    return d
+
+
+@dataclass
+class PackedWeight:
+    """A weight in the device layout (three uint8 device buffers) plus its shape."""
+    fmt: int
+    N: int
+    K: int
+    group: int
+    has_zeros: int
+    w: torch.Tensor
+    s: torch.Tensor
+    aux: torch.Tensor | None
+
+    @property
+    def device(self) -> torch.device:
+        return self.w.device
+
+
+def packed_bytes(fmt, N: int, K: int, group: int, has_zeros: bool = False):
+    """(w_bytes, s_bytes, aux_bytes) of the device layout."""
+    w, s, a = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qlinear_packed_bytes(_fmt(fmt), N, K, group, int(has_zeros), ctypes.byref(w), ctypes.byref(s),
+                                      ctypes.byref(a)), "qlinear_packed_bytes")
+    return w.value, s.value, a.value
+
+
+def pack(fmt, N: int, K: int, group: int, codes: torch.Tensor, scales: torch.Tensor, aux=None) -> PackedWeight:
+    """Pack canonical device tensors (see include/qlinear.h) into the device layout.
+
+    codes: uint8 [N, K/2] (4-bit formats) or int8 [N, K] (INT8); scales: float16 [N, K/G]
+    (INT4), bfloat16 [N, K/G] (INT8), uint8 [N, K/32] (MXFP4), bfloat16 [N] norms (CB4);
+    aux: uint8 zeros [N, K/G] (INT4 with zero-point, device) or 16 float32 centroids
+    (CB4, host sequence or CPU tensor)."""
+    f = _fmt(fmt)
+    dev = codes.device
+    has_zeros = 1 if (f == QL_INT4 and aux is not None) else 0
+    wb, sb, ab = packed_bytes(f, N, K, group, bool(has_zeros))
+    w = torch.empty(wb, dtype=torch.uint8, device=dev)
+    s = torch.empty(sb, dtype=torch.uint8, device=dev)
+    a = torch.empty(ab, dtype=torch.uint8, device=dev) if ab else None
+    codes = codes.contiguous()
+    scales = scales.contiguous()
+    aux_ptr = None
+    keep = None
+    if f == QL_CB4:
+        keep = torch.as_tensor(aux, dtype=torch.float32).cpu().contiguous()
+        if keep.numel() != 16:
+            raise QLinearError("a codebook has 16 centroids")
+        aux_ptr = keep.data_ptr()
+    elif aux is not None:
+        aux = aux.contiguous()
+        aux_ptr = aux.data_ptr()
+    _check(lib().qlinear_pack(f, N, K, group, _ptr(codes), _ptr(scales), aux_ptr, _ptr(w), _ptr(s), _ptr(a),
+                              _stream(dev)), "qlinear_pack")
+    return PackedWeight(f, N, K, group, has_zeros, w, s, a)
+
+
+def unpack(pw: PackedWeight):
+    """Device layout -> canonical (codes, scales, aux) device tensors."""
+    f, N, K, G = pw.fmt, pw.N, pw.K, pw.group
+    dev = pw.device
+    if f == QL_INT8:
+        codes = torch.empty((N, K), dtype=torch.int8, device=dev)
+    else:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    if f == QL_INT4:
+        scales = torch.empty((N, K // G), dtype=torch.float16, device=dev)
+    elif f == QL_INT8:
+        scales = torch.empty((N, K // G), dtype=torch.bfloat16, device=dev)
+    elif f == QL_MXFP4:
+        scales = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    else:
+        scales = torch.empty((N,), dtype=torch.bfloat16, device=dev)
+    aux = None
+    if f == QL_INT4 and pw.has_zeros:
+        aux = torch.empty((N, K // G), dtype=torch.uint8, device=dev)
+    elif f == QL_CB4:
+        aux = torch.empty((16,), dtype=torch.float32, device=dev)
+    _check(lib().qlinear_unpack(f, N, K, G, pw.has_zeros, _ptr(pw.w), _ptr(pw.s), _ptr(pw.aux), _ptr(codes),
+                                _ptr(scales), _ptr(aux), _stream(dev)), "qlinear_unpack")
+    return codes, scales, aux
+
+
+def dequant_tile(pw: PackedWeight, n0: int = 0, k0: int = 0, tn: int | None = None, tk: int | None = None,
+                 mode: int = 0) -> torch.Tensor:
+    """float32 [tn, tk] dump of D(W) (mode 0) or of the bf16 matrix-core operand (mode 1)."""
+    tn = pw.N - n0 if tn is None else tn
+    tk = pw.K - k0 if tk is None else tk
+    out = torch.empty((tn, tk), dtype=torch.float32, device=pw.device)
+    _check(lib().qlinear_dequant_tile(pw.fmt, pw.N, pw.K, pw.group, pw.has_zeros, _ptr(pw.w), _ptr(pw.s),
+                                      _ptr(pw.aux), n0, k0, tn, tk, mode, _ptr(out), _stream(pw.device)),
+           "qlinear_dequant_tile")
+    return out
+
+
+def workspace_bytes(fmt, M: int, N: int, K: int, group: int, act=None) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().qlinear_workspace_bytes(_fmt(fmt), M, N, K, group, _ACT[act], ctypes.byref(b)),
+           "qlinear_workspace_bytes")
+    return b.value
+
+
+def linear(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, act=None,
+           out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = A . D(Wq)^T + b for bf16 x [..., K] (or [..., 2K] = [up | gate] with act="swiglu").
+
+    Inference only: inputs that require grad are rejected."""
+    if x.requires_grad or (bias is not None and bias.requires_grad):
+        raise QLinearError("inference-only operator: inputs must not require grad")
+    if x.device.type != "cuda" or pw.w.device.type != "cuda":
+        raise QLinearError("the library runs on a HIP device only")
+    if x.dtype != torch.bfloat16:
+        raise QLinearError("x must be bfloat16")
+    act_id = _ACT[act]
+    width = 2 * pw.K if act_id == 1 else pw.K
+    if x.shape[-1] != width:
+        raise QLinearError(f"x has {x.shape[-1]} features, expected {width}")
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, width)
+    if not x2.is_contiguous():
+        x2 = x2.contiguous()
+    M = x2.shape[0]
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != pw.N):
+        raise QLinearError("bias must be bfloat16 [N]")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise QLinearError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=out_dtype, device=x.device)
+    ws_need = workspace_bytes(pw.fmt, M, pw.N, pw.K, pw.group, act)
+    if ws_need and (workspace is None or workspace.numel() < ws_need):
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=x.device)
+    _check(lib().qlinear_forward(_ptr(x2), M, pw.N, pw.K, _ptr(pw.w), _ptr(pw.s), _ptr(pw.aux), pw.fmt, pw.group,
+                                 pw.has_zeros, _ptr(bias), act_id, _ptr(out), 1 if out_dtype == torch.float32 else 0,
+                                 _ptr(workspace) if ws_need else None, ws_need, _stream(x.device)),
+           "qlinear_forward")
+    return out.reshape(*lead, pw.N)

@@ -1,0 +1,240 @@
+// C ABI of the library: argument validation, sizes, schedule choice and launches.
+// Every check runs before anything is queued, so an error leaves all outputs untouched.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/qlinear.h"
+#include "ql_common.hpp"
+#include "ql_decode.hpp"
+#include "ql_launch.hpp"
+
+namespace ql {
+
+// The schedule is a pure function of the shape: it assumes the 256 compute units of
+// the MI355X / MI350X (gfx950), so workspace sizes can be queried without a device.
+constexpr int PLAN_CUS = 256;
+
+namespace {
+
+// Split-K reduction in a fixed order (s = 0, 1, ...), then the epilogue.
+__global__ void __launch_bounds__(256) qreduce_kernel(GemmArgs a) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= int64_t(a.M) * a.N) return;
+    const int m = int(idx / a.N), n = int(idx % a.N);
+    float v = 0.0f;
+    for (int s = 0; s < a.ks; ++s) v += a.ws[(int64_t(s) * a.M + m) * a.Np + n];
+    if (a.aux) {
+        // codebook (aux is only passed for CB4): row scale times 1/alpha
+        v *= reinterpret_cast<const float *>(a.s)[n] * reinterpret_cast<const CbRecord *>(a.aux)->inv_alpha;
+    }
+    if (a.bias) v += bf16_bits_to_f32(a.bias[n]);
+    if (a.out_f32) reinterpret_cast<float *>(a.out)[idx] = v;
+    else reinterpret_cast<__bf16 *>(a.out)[idx] = (__bf16)v;
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const Layout &, const Plan &, const GemmArgs &a, hipStream_t st) {
+    const int64_t n = int64_t(a.M) * a.N;
+    hipLaunchKernelGGL(qreduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace ql
+
+using namespace ql;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape / format validation shared by every entry point.
+ql_status check_format(ql_format f, int64_t N, int64_t K, int group, int has_zeros) {
+    if (f < QL_INT4 || f > QL_CB4) return QL_E_ARG;
+    if (has_zeros != 0 && has_zeros != 1) return QL_E_ARG;
+    if (has_zeros && f != QL_INT4) return QL_E_ARG;
+    if (N <= 0 || K <= 0 || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 30)) return QL_E_SHAPE;
+    if (K % 32 != 0) return QL_E_SHAPE;
+    if (f == QL_INT4 || f == QL_INT8) {
+        if (group != 32 && group != 64 && group != 128 && group != 256) return QL_E_SHAPE;
+        if (K % group != 0) return QL_E_SHAPE;
+    } else if (f == QL_MXFP4) {
+        if (group != 32) return QL_E_SHAPE;
+    }
+    const Layout L = make_layout(int(f), N, K, f == QL_CB4 ? 0 : group, has_zeros != 0);
+    // 32-bit buffer offsets inside the kernels
+    if (L.w_bytes >= (size_t(1) << 32) || L.s_bytes >= (size_t(1) << 32)) return QL_E_SHAPE;
+    return QL_OK;
+}
+
+Layout layout_of(ql_format f, int64_t N, int64_t K, int group, int has_zeros) {
+    return make_layout(int(f), N, K, f == QL_CB4 ? 0 : group, has_zeros != 0);
+}
+
+ql_status from_hip(hipError_t e) { return e == hipSuccess ? QL_OK : QL_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int qlinear_version(void) { return 0x000100; }
+
+const char *qlinear_error_string(ql_status s) {
+    switch (s) {
+        case QL_OK: return "ok";
+        case QL_E_ARG: return "invalid argument";
+        case QL_E_SHAPE: return "unsupported shape or group size";
+        case QL_E_ALIGN: return "misaligned pointer";
+        case QL_E_UNSUPPORTED: return "unsupported combination";
+        case QL_E_WORKSPACE: return "workspace too small";
+        case QL_E_HIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+ql_status qlinear_packed_bytes(ql_format f, int64_t N, int64_t K, int group, int has_zeros, size_t *w_bytes,
+                               size_t *s_bytes, size_t *aux_bytes) {
+    if (!w_bytes || !s_bytes || !aux_bytes) return QL_E_ARG;
+    const ql_status st = check_format(f, N, K, group, has_zeros);
+    if (st != QL_OK) return st;
+    const Layout L = layout_of(f, N, K, group, has_zeros);
+    *w_bytes = L.w_bytes;
+    *s_bytes = L.s_bytes;
+    *aux_bytes = L.aux_bytes;
+    return QL_OK;
+}
+
+ql_status qlinear_pack(ql_format f, int64_t N, int64_t K, int group, const void *codes, const void *scales,
+                       const void *aux_in, void *packed_w, void *packed_s, void *packed_aux, void *stream) {
+    const int has_zeros = (f == QL_INT4 && aux_in != nullptr) ? 1 : 0;
+    ql_status st = check_format(f, N, K, group, has_zeros);
+    if (st != QL_OK) return st;
+    if (!codes || !scales || !packed_w || !packed_s) return QL_E_ARG;
+    if ((f == QL_CB4) && (!aux_in || !packed_aux)) return QL_E_ARG;
+    if (f == QL_INT4 && has_zeros && !packed_aux) return QL_E_ARG;
+    if ((f == QL_INT8 || f == QL_MXFP4) && aux_in) return QL_E_ARG;
+    if (!aligned(codes, f == QL_INT8 ? 8 : 4)) return QL_E_ALIGN;
+    if (!aligned(scales, f == QL_MXFP4 ? 1 : 2)) return QL_E_ALIGN;
+    if (!aligned(packed_w, 16) || !aligned(packed_s, 16) || (packed_aux && !aligned(packed_aux, 16))) return QL_E_ALIGN;
+    if (f == QL_CB4) {
+        const float *c = static_cast<const float *>(aux_in);
+        for (int j = 0; j < 16; ++j) {
+            if (!isfinite(c[j])) return QL_E_UNSUPPORTED;
+            if (c[15 - j] != -c[j]) return QL_E_UNSUPPORTED;   // sign-magnitude decode needs symmetry
+        }
+    }
+    const Layout L = layout_of(f, N, K, group, has_zeros);
+    return from_hip(launch_pack(L, codes, scales, aux_in, packed_w, packed_s, packed_aux, (hipStream_t)stream));
+}
+
+ql_status qlinear_unpack(ql_format f, int64_t N, int64_t K, int group, int has_zeros, const void *packed_w,
+                         const void *packed_s, const void *packed_aux, void *codes, void *scales, void *aux_out,
+                         void *stream) {
+    ql_status st = check_format(f, N, K, group, has_zeros);
+    if (st != QL_OK) return st;
+    if (!codes || !scales || !packed_w || !packed_s) return QL_E_ARG;
+    const bool needs_aux = (f == QL_CB4) || (f == QL_INT4 && has_zeros);
+    if (needs_aux && (!packed_aux || !aux_out)) return QL_E_ARG;
+    if (!aligned(codes, f == QL_INT8 ? 8 : 4)) return QL_E_ALIGN;
+    if (!aligned(scales, f == QL_MXFP4 ? 1 : 2)) return QL_E_ALIGN;
+    if (!aligned(packed_w, 16) || !aligned(packed_s, 16) || (packed_aux && !aligned(packed_aux, 16))) return QL_E_ALIGN;
+    if (f == QL_CB4 && !aligned(aux_out, 4)) return QL_E_ALIGN;
+    const Layout L = layout_of(f, N, K, group, has_zeros);
+    return from_hip(launch_unpack(L, packed_w, packed_s, packed_aux, codes, scales, aux_out, (hipStream_t)stream));
+}
+
+ql_status qlinear_dequant_tile(ql_format f, int64_t N, int64_t K, int group, int has_zeros, const void *packed_w,
+                               const void *packed_s, const void *packed_aux, int64_t n0, int64_t k0, int64_t tn,
+                               int64_t tk, int mode, float *out, void *stream) {
+    ql_status st = check_format(f, N, K, group, has_zeros);
+    if (st != QL_OK) return st;
+    if (!packed_w || !packed_s || !out) return QL_E_ARG;
+    if (((f == QL_CB4) || (f == QL_INT4 && has_zeros)) && !packed_aux) return QL_E_ARG;
+    if (mode != 0 && mode != 1) return QL_E_ARG;
+    if (n0 < 0 || k0 < 0 || tn < 0 || tk < 0 || n0 + tn > N || k0 + tk > K) return QL_E_SHAPE;
+    if (tn * tk >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    if (!aligned(packed_w, 16) || !aligned(packed_s, 16) || !aligned(out, 4)) return QL_E_ALIGN;
+    if (tn == 0 || tk == 0) return QL_OK;
+    const Layout L = layout_of(f, N, K, group, has_zeros);
+    return from_hip(launch_dequant_tile(L, packed_w, packed_s, packed_aux, n0, k0, tn, tk, mode, out,
+                                        (hipStream_t)stream));
+}
+
+ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, int group, ql_act act,
+                                  size_t *bytes) {
+    if (!bytes) return QL_E_ARG;
+    if (act != QL_ACT_NONE && act != QL_ACT_SWIGLU) return QL_E_ARG;
+    if (M < 0 || M >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    ql_status st = check_format(f, N, K, group, 0);
+    if (st != QL_OK) return st;
+    if (M == 0) {
+        *bytes = 0;
+        return QL_OK;
+    }
+    const Layout L = layout_of(f, N, K, group, 0);
+    *bytes = make_plan(L, M, PLAN_CUS).ws_bytes;
+    return QL_OK;
+}
+
+ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K, const void *packed_w, const void *packed_s,
+                          const void *packed_aux, ql_format f, int group, int has_zeros, const void *bias, ql_act act,
+                          void *out, ql_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    ql_status st = check_format(f, N, K, group, has_zeros);
+    if (st != QL_OK) return st;
+    if (act != QL_ACT_NONE && act != QL_ACT_SWIGLU) return QL_E_ARG;
+    if (out_dtype != QL_BF16 && out_dtype != QL_F32) return QL_E_ARG;
+    if (M < 0 || M >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    const int64_t ldx = act == QL_ACT_SWIGLU ? 2 * K : K;
+    if (M * ldx >= (int64_t(1) << 31) || M * N >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    if (M == 0) return QL_OK;
+    if (!x || !packed_w || !packed_s || !out) return QL_E_ARG;
+    if (((f == QL_CB4) || (f == QL_INT4 && has_zeros)) && !packed_aux) return QL_E_ARG;
+    if (!aligned(x, 16) || !aligned(packed_w, 16) || !aligned(packed_s, 16)) return QL_E_ALIGN;
+    if (packed_aux && !aligned(packed_aux, 16)) return QL_E_ALIGN;
+    if (bias && !aligned(bias, 2)) return QL_E_ALIGN;
+    if (!aligned(out, out_dtype == QL_F32 ? 4 : 2)) return QL_E_ALIGN;
+    const Layout L = layout_of(f, N, K, group, has_zeros);
+    const Plan p = make_plan(L, M, PLAN_CUS);
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes) return QL_E_WORKSPACE;
+        if (!aligned(workspace, 16)) return QL_E_ALIGN;
+    }
+    GemmArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = static_cast<const uint8_t *>(packed_w);
+    a.s = static_cast<const uint8_t *>(packed_s);
+    a.z = (f == QL_INT4 && has_zeros) ? static_cast<const uint8_t *>(packed_aux) : nullptr;
+    a.aux = (f == QL_CB4) ? static_cast<const uint8_t *>(packed_aux) : nullptr;
+    a.bias = static_cast<const uint16_t *>(bias);
+    a.out = out;
+    a.ws = static_cast<float *>(workspace);
+    a.M = int(M);
+    a.N = int(N);
+    a.K = int(K);
+    a.ldx = int(ldx);
+    a.Np = int(L.Np);
+    a.ntiles = int(L.ntiles);
+    a.kchunks = int(L.kchunks);
+    a.ngroups = int(L.ngroups);
+    a.cps = p.cps;
+    a.ks = p.ks;
+    a.swiglu = act == QL_ACT_SWIGLU ? 1 : 0;
+    a.out_f32 = out_dtype == QL_F32 ? 1 : 0;
+    a.w_bytes = uint32_t(L.w_bytes);
+    a.s_bytes = uint32_t(L.s_bytes);
+    a.z_bytes = uint32_t(L.aux_bytes);
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (f) {
+        case QL_INT4: e = launch_gemm_int4(L, p, a, s); break;
+        case QL_INT8: e = launch_gemm_int8(L, p, a, s); break;
+        case QL_MXFP4: e = launch_gemm_mxfp4(L, p, a, s); break;
+        default: e = launch_gemm_cb4(L, p, a, s); break;
+    }
+    if (e != hipSuccess) return QL_E_HIP;
+    if (p.ks > 1) e = launch_reduce(L, p, a, s);
+    return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Register-level decode of one packed k-step (8 inputs of one column) into the eight
+// bf16 values a lane feeds to v_mfma_f32_16x16x32_bf16 as its B operand.
+//
+// The B operand is always an exact bf16 image of the code:
+//   INT4   offset-binary code u in 0..15  ->  bf16(128 + u)       (one AND-OR per pair)
+//   INT8   offset-binary code u in 0..255 ->  bf16(u)             (byte -> f32 -> bf16)
+//   MXFP4  E2M1 code with its E8M0 scale  ->  bf16(e2m1 * 2^(e-127))  (hardware convert)
+//   CB4    sign-magnitude index           ->  +-bf16(alpha * c[8 + m])  (byte permutes)
+// Offsets, group scales, zero-points and codebook row scales are applied to the
+// float32 accumulators, so no rounding happens before the matrix cores except the
+// single bf16 rounding of alpha * c for the codebook.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ql_common.hpp"
+
+namespace ql {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer descriptor word 3 for gfx9-family parts (untyped 32-bit data format).
+constexpr int BUF_DWORD3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, BUF_DWORD3);
+}
+
+// Ranged loads: a byte offset at or beyond the descriptor's size reads as zero.
+__device__ inline u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ inline uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ inline uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ inline uint32_t ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+__device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ inline float f16_bits_to_f32(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- bit position of element j (0..7) of a k-step inside its 32-bit word -------------
+// INT4: pairs (2p, 2p+1) sit at bits 4p and 16+4p, so one shift and one AND-OR give the
+// packed bf16 pair.  CB4: the four low nibbles of the bytes hold elements 0,2,1,3 and the
+// high nibbles 4,6,5,7, so a byte permute gathers the pairs.  MXFP4: natural order.
+__host__ __device__ constexpr int pos_int4(int j) { return 4 * (j >> 1) + 16 * (j & 1); }
+__host__ __device__ constexpr int pos_cb4(int j) {
+    return 8 * (((j & 1) << 1) | ((j >> 1) & 1)) + 4 * (j >> 2);
+}
+__host__ __device__ constexpr int pos_mxfp4(int j) { return 4 * j; }
+
+// ---- INT4: bf16 bit pattern 0x4300 | u is exactly 128 + u ------------------------------
+__device__ inline u32x4 dec_int4(uint32_t w) {
+    const uint32_t m = 0x000F000Fu, e = 0x43004300u;
+    u32x4 r;
+    r.x = (w & m) | e;
+    r.y = ((w >> 4) & m) | e;
+    r.z = ((w >> 8) & m) | e;
+    r.w = ((w >> 12) & m) | e;
+    return r;
+}
+
+// ---- INT8: eight offset-binary bytes (two words) -> bf16(u), exact for u <= 255 ---------
+__device__ inline u32x4 dec_int8(uint32_t d0, uint32_t d1) {
+    u32x4 r;
+    r.x = pack_bf16x2((float)(d0 & 0xFFu), (float)((d0 >> 8) & 0xFFu));
+    r.y = pack_bf16x2((float)((d0 >> 16) & 0xFFu), (float)(d0 >> 24));
+    r.z = pack_bf16x2((float)(d1 & 0xFFu), (float)((d1 >> 8) & 0xFFu));
+    r.w = pack_bf16x2((float)((d1 >> 16) & 0xFFu), (float)(d1 >> 24));
+    return r;
+}
+
+// ---- MXFP4: E8M0 code -> float32 scale 2^(e-127); code 0 is the subnormal 2^-127 -------
+__device__ inline float e8m0_to_f32(uint32_t e) {
+    return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+__device__ inline u32x4 dec_mxfp4(uint32_t w, float scale) {
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    return r;
+}
+
+// ---- CB4: magnitude LUT of 8 bf16 values split into low-byte and high-byte planes ------
+struct CbLut {
+    uint32_t lo0, lo1, hi0, hi1;   // byte m of lo0/lo1 (m < 4 / m >= 4) = low byte of entry m
+};
+
+__device__ inline u32x4 dec_cb4(uint32_t w, const CbLut &L) {
+    const uint32_t sa = w & 0x07070707u;          // magnitudes of elements 0,2,1,3
+    const uint32_t sb = (w >> 4) & 0x07070707u;   // magnitudes of elements 4,6,5,7
+    const uint32_t ha = __builtin_amdgcn_perm(L.hi1, L.hi0, sa);
+    const uint32_t la = __builtin_amdgcn_perm(L.lo1, L.lo0, sa);
+    const uint32_t hb = __builtin_amdgcn_perm(L.hi1, L.hi0, sb);
+    const uint32_t lb = __builtin_amdgcn_perm(L.lo1, L.lo0, sb);
+    const uint32_t sg = 0x80008000u;
+    u32x4 r;
+    r.x = __builtin_amdgcn_perm(ha, la, 0x06020400u) ^ ((w << 12) & sg);   // elements 0, 1
+    r.y = __builtin_amdgcn_perm(ha, la, 0x07030501u) ^ ((w << 4) & sg);    // elements 2, 3
+    r.z = __builtin_amdgcn_perm(hb, lb, 0x06020400u) ^ ((w << 8) & sg);    // elements 4, 5
+    r.w = __builtin_amdgcn_perm(hb, lb, 0x07030501u) ^ (w & sg);           // elements 6, 7
+    return r;
+}
+
+// Codebook record (128 bytes) written by the packer:
+//   [0, 64)   float32 centroids c[16] as given
+//   [64, 80)  CbLut planes of bf16(alpha * c[8 + m]), m = 0..7
+//   [80, 84)  float32 1/alpha
+//   [84, 88)  float32 alpha
+struct CbRecord {
+    float centroids[16];
+    CbLut lut;
+    float inv_alpha;
+    float alpha;
+    uint32_t pad[10];
+};
+static_assert(sizeof(CbRecord) == CB_AUX_BYTES, "codebook record size");
+
+// Canonical index j <-> sign-magnitude nibble (bit 3 = sign, bits 0..2 = m) for a
+// symmetric codebook (c[15 - j] == -c[j]): j >= 8 is +c[8 + m]; j < 8 is -c[8 + m], m = 7 - j.
+__host__ __device__ inline uint32_t cb_index_to_nibble(uint32_t j) { return j >= 8 ? j - 8 : 8u | (7u - j); }
+__host__ __device__ inline uint32_t cb_nibble_to_index(uint32_t n) { return (n & 8u) ? 7u - (n & 7u) : 8u + n; }
+
+}  // namespace ql

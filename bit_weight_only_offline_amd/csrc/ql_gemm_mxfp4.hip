@@ -1,0 +1,9 @@
+// MXFP4 instantiations of the linear kernel.
+#include "ql_gemm_dispatch.hpp"
+#include "ql_launch.hpp"
+
+namespace ql {
+hipError_t launch_gemm_mxfp4(const Layout &, const Plan &p, const GemmArgs &a, hipStream_t st) {
+    return launch_qmm_cfg<FMT_MXFP4, false, 1>(p, a, st);
+}
+}  // namespace ql

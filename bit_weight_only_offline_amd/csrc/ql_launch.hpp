@@ -1,0 +1,24 @@
+// Host-side launchers shared between the translation units of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ql_common.hpp"
+
+namespace ql {
+
+hipError_t launch_pack(const Layout &L, const void *codes, const void *scales, const void *aux_in,
+                       void *pw, void *ps, void *paux, hipStream_t st);
+hipError_t launch_unpack(const Layout &L, const void *pw, const void *ps, const void *paux,
+                         void *codes, void *scales, void *aux_out, hipStream_t st);
+hipError_t launch_dequant_tile(const Layout &L, const void *pw, const void *ps, const void *paux, int64_t n0,
+                               int64_t k0, int64_t tn, int64_t tk, int mode, float *out, hipStream_t st);
+
+// One translation unit per format family keeps the template instantiations apart.
+hipError_t launch_gemm_int4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_int8(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_mxfp4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_cb4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
+hipError_t launch_reduce(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
+
+}  // namespace ql

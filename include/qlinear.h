@@ -1,0 +1,171 @@
+/*
+ * qlinear.h -- C ABI of the MI355X (gfx950) weight-only low-bit linear layer
+ *
+ *     Y[M, N] = A[M, K] . D(Wq)[N, K]^T + b[N]
+ *
+ * A is the bf16 activation X, or h = up * silu(gate) formed from a raw bf16 input
+ * [M, 2K] = [up | gate] (piper-kernels 0.2.1 package description, section
+ * "ConvRot INT8": convrot_linear(..., input_activation="swiglu") on a [.., 2*in]
+ * input).  D(Wq) is the weight decoded from one of four packed formats; it is decoded
+ * in registers inside the kernels and never written out as a dense matrix (OrbitQuant
+ * Packed Matmul model card, "API": no dequantized weight cache; AutoRound Kernel
+ * package description, "1. Linear": woqgemm on a packed blob).
+ *
+ * Formats (canonical, i.e. checkpoint, layouts; N = out_features, K = in_features):
+ *
+ *   QL_INT4   codes  uint8 [N, K/2]  two 4-bit codes per byte, even k in the low nibble
+ *                                    (selective_state_update_pairnib.py, pack_pairnib);
+ *                                    two's complement q in [-8, 7] when symmetric,
+ *                                    unsigned q in [0, 15] with a zero-point
+ *             scales fp16  [N, K/G]  G in {32, 64, 128, 256}
+ *             zeros  uint8 [N, K/G]  0..15, or NULL for symmetric.   w = s*q  or  s*(q - z)
+ *             (AutoRound Kernel, "1. Linear", "Example": qweight, scale and zp per group;
+ *              "Supported Data Types": sym / asym)
+ *   QL_MXFP4  codes  uint8 [N, K/2]  E2M1 codes (sign, 2 exponent bits bias 1, 1 mantissa)
+ *             scales uint8 [N, K/32] E8M0 codes c -> 2^(c-127); G must be 32
+ *             (Petit package description, "Features": MXFP4 weights)
+ *   QL_INT8   codes  int8  [N, K]    q in [-128, 127]
+ *             scales bf16  [N, K/G]  G in {32, 64, 128, 256}; 256 is ConvRot's group
+ *             (piper-kernels, "ConvRot INT8": group_size=256, logical_dtype=bfloat16)
+ *   QL_CB4    codes  uint8 [N, K/2]  4-bit indices into a 16-entry codebook
+ *             scales bf16  [N]       row norms;  w = c[idx] * norm_n / sqrt(K)
+ *             aux    fp32  [16]      centroids, symmetric: c[15-j] == -c[j]
+ *             (OrbitQuant card, "API": packed indices, row norms, Lloyd-Max centroids)
+ *
+ * qlinear_pack() shuffles a canonical weight once, offline, into the device layout
+ * that the kernels stream with coalesced 16-byte loads (Petit package description,
+ * "Techniques and performance": weights shuffled offline so that on-GPU
+ * dequantisation is cheap).  qlinear_unpack() inverts it bit-exactly.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless an argument says "host".  The caller
+ *     allocates and owns every buffer; the library allocates no device memory and
+ *     keeps no device state.  Sizes come from qlinear_packed_bytes() and
+ *     qlinear_workspace_bytes().
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is queued
+ *     on it asynchronously; no entry point synchronises or copies device memory to
+ *     the host.
+ *   - Every argument is validated before anything is queued: an error return leaves
+ *     all outputs untouched.  QL_E_HIP reports a failed launch.
+ *   - Entry points are reentrant; concurrent calls on different streams are safe
+ *     when their output buffers do not overlap.
+ *   - Device pointers must be 16-byte aligned (x, packed buffers, workspace) or
+ *     aligned to their element size (bias, out, canonical arrays).
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QL_OK = 0,
+    QL_E_ARG = 1,          /* NULL where a buffer is required, unknown enum value    */
+    QL_E_SHAPE = 2,        /* negative size, K not a multiple of 32 or of the group,
+                              unsupported group size for the format                  */
+    QL_E_ALIGN = 3,        /* a pointer is not aligned as required                    */
+    QL_E_UNSUPPORTED = 4,  /* a combination the kernels do not implement (e.g. an
+                              asymmetric codebook); never a silent fallback          */
+    QL_E_WORKSPACE = 5,    /* workspace smaller than qlinear_workspace_bytes()        */
+    QL_E_HIP = 6           /* a HIP launch failed                                     */
+} ql_status;
+
+typedef enum { QL_INT4 = 0, QL_MXFP4 = 1, QL_INT8 = 2, QL_CB4 = 3 } ql_format;
+typedef enum { QL_ACT_NONE = 0, QL_ACT_SWIGLU = 1 } ql_act;
+typedef enum { QL_BF16 = 0, QL_F32 = 1 } ql_dtype;
+
+/* Library version, e.g. 0x000100 for 0.1.0. */
+int qlinear_version(void);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *qlinear_error_string(ql_status s);
+
+/*
+ * Bytes of the three device-layout buffers of a packed weight.
+ *   f, N, K, group  as above (group is ignored for QL_CB4 and must be 32 for QL_MXFP4)
+ *   has_zeros       1 for INT4 with a zero-point, else 0
+ *   w_bytes         packed codes
+ *   s_bytes         packed scales (CB4: float32 row scales and bf16 norms)
+ *   aux_bytes       packed zero-points (INT4 with zeros), codebook record (CB4, 128 B),
+ *                   else 0
+ * All three are multiples of 256.  Host-only: touches no device.
+ */
+ql_status qlinear_packed_bytes(ql_format f, int64_t N, int64_t K, int group, int has_zeros,
+                               size_t *w_bytes, size_t *s_bytes, size_t *aux_bytes);
+
+/*
+ * Offline pack: canonical arrays -> device layout (one kernel launch per buffer).
+ *   codes   canonical codes (see the format table)
+ *   scales  canonical scales (CB4: bf16 row norms [N])
+ *   aux_in  INT4: zeros uint8 [N, K/G] or NULL (symmetric); CB4: HOST pointer to the 16
+ *           float32 centroids, read during the call; otherwise must be NULL
+ *   packed_w, packed_s, packed_aux   outputs sized by qlinear_packed_bytes()
+ *           (packed_aux may be NULL when aux_bytes is 0)
+ * CB4 also chooses a per-codebook multiplier alpha in [1, 2) that minimises the bf16
+ * rounding error of alpha * c[j] and records it in packed_aux.
+ * Errors: QL_E_UNSUPPORTED for a codebook that is not symmetric or not finite.
+ */
+ql_status qlinear_pack(ql_format f, int64_t N, int64_t K, int group,
+                       const void *codes, const void *scales, const void *aux_in,
+                       void *packed_w, void *packed_s, void *packed_aux, void *stream);
+
+/*
+ * Inverse of qlinear_pack(): device layout -> canonical arrays, bit-exact.
+ *   codes, scales   canonical outputs
+ *   aux_out         INT4 with zeros: zeros [N, K/G]; CB4: float32 centroids [16]
+ *                   (device); otherwise NULL
+ *   has_zeros       INT4 only: 1 if packed_aux holds zero-points
+ */
+ql_status qlinear_unpack(ql_format f, int64_t N, int64_t K, int group, int has_zeros,
+                         const void *packed_w, const void *packed_s, const void *packed_aux,
+                         void *codes, void *scales, void *aux_out, void *stream);
+
+/*
+ * Debug dump of a dequantised weight tile, decoded by the same register-level code
+ * the GEMM kernels use.
+ *   n0, k0, tn, tk  tile origin and extent (0 <= n0, n0+tn <= N, same for k)
+ *   mode 0          out = D(Wq)[n0.., k0..] in float32, exactly as the format defines it
+ *   mode 1          out = the bf16 operand the matrix cores receive, widened to float32
+ *                   (before group, zero-point and codebook row scaling)
+ *   out             float32 [tn, tk] row-major
+ */
+ql_status qlinear_dequant_tile(ql_format f, int64_t N, int64_t K, int group, int has_zeros,
+                               const void *packed_w, const void *packed_s, const void *packed_aux,
+                               int64_t n0, int64_t k0, int64_t tn, int64_t tk, int mode,
+                               float *out, void *stream);
+
+/*
+ * Workspace that qlinear_forward() needs for this shape (split-K partial sums);
+ * 0 when the chosen schedule reduces inside the kernel.  Host-only.
+ */
+ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, int group,
+                                  ql_act act, size_t *bytes);
+
+/*
+ * The linear layer.
+ *   x          bf16 [M, K] (act = NONE) or [M, 2K] = [up | gate] (act = SWIGLU), row-major
+ *   M          rows (0 is a no-op); N, K, group as packed
+ *   packed_w, packed_s, packed_aux   from qlinear_pack() (packed_aux NULL for INT4
+ *              symmetric, INT8 and MXFP4)
+ *   bias       bf16 [N] or NULL
+ *   out        [M, N] row-major, bf16 (RNE of the float32 result) or float32
+ *   workspace  device buffer of at least qlinear_workspace_bytes() (may be NULL if 0)
+ * The path is chosen by M: a split-K streaming schedule for decode-sized M and an
+ * LDS-staged matrix-core tile schedule for larger M; both accumulate in float32 and
+ * reduce split-K partials in a fixed order, so results are run-to-run identical.
+ */
+ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K,
+                          const void *packed_w, const void *packed_s, const void *packed_aux,
+                          ql_format f, int group, int has_zeros,
+                          const void *bias, ql_act act, void *out, ql_dtype out_dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

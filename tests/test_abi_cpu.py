@@ -1,0 +1,142 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/qlinear.h declares, sizes its buffers as documented and rejects invalid
+arguments before queuing any work (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+
+QL_OK, QL_E_ARG, QL_E_SHAPE, QL_E_ALIGN, QL_E_UNSUPPORTED, QL_E_WORKSPACE, QL_E_HIP = range(7)
+INT4, MXFP4, INT8, CB4 = range(4)
+FAKE = 1 << 20          # an aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    import bit_weight_only_offline_amd as Q
+    return Q.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qlinear_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.qlinear_version() == 0x000100
+
+
+def test_error_strings(L):
+    for s in range(7):
+        assert L.qlinear_error_string(s)
+    assert L.qlinear_error_string(99) == b"unknown status"
+
+
+def _sizes(L, f, N, K, G, z):
+    w, s, a = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = L.qlinear_packed_bytes(f, N, K, G, z, ctypes.byref(w), ctypes.byref(s), ctypes.byref(a))
+    return st, w.value, s.value, a.value
+
+
+def test_packed_bytes_layout(L):
+    # INT4 4096 x 4096, group 128 with zeros: 256 column tiles x 32 chunks x 1 KiB,
+    # fp16 scales [256][32][16], 4-bit zeros [256][32][8 bytes]
+    assert _sizes(L, INT4, 4096, 4096, 128, 1) == (QL_OK, 8388608, 262144, 65536)
+    # MXFP4 28672 x 4096: one 32-bit word of four E8M0 codes per column and chunk
+    assert _sizes(L, MXFP4, 28672, 4096, 32, 0) == (QL_OK, 1792 * 32 * 1024, 1792 * 32 * 64, 0)
+    # INT8 8192 x 28672 group 256: chunks of 64 inputs, bf16 scales
+    assert _sizes(L, INT8, 8192, 28672, 256, 0) == (QL_OK, 512 * 448 * 1024, 512 * 112 * 32, 0)
+    # CB4 3072 x 3072: float32 row scales + bf16 norms, 128-byte codebook record
+    assert _sizes(L, CB4, 3072, 3072, 0, 0) == (QL_OK, 192 * 24 * 1024, 3072 * 6, 128)
+    # ragged N and K are padded to whole tiles / chunks (and 256-byte multiples)
+    st, w, s, a = _sizes(L, INT4, 50, 448, 32, 1)
+    assert st == QL_OK and w == 4 * 4 * 1024 and s == 4 * 16 * 32 and a == 512
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 64, 64, 32, 0), QL_E_ARG),           # unknown format
+    ((INT4, 64, 48, 32, 0), QL_E_SHAPE),      # K not a multiple of 32
+    ((INT4, 64, 256, 48, 0), QL_E_SHAPE),     # unsupported group
+    ((INT4, 64, 320, 128, 0), QL_E_SHAPE),    # K not a multiple of the group
+    ((MXFP4, 64, 256, 64, 0), QL_E_SHAPE),    # MXFP4 blocks are 32
+    ((INT8, 64, 256, 256, 1), QL_E_ARG),      # zero-points only for INT4
+    ((INT4, 0, 256, 128, 0), QL_E_SHAPE),     # empty weight
+    ((INT4, -5, 256, 128, 0), QL_E_SHAPE),
+])
+def test_packed_bytes_rejects(L, args, code):
+    assert _sizes(L, *args)[0] == code
+
+
+def _fwd(L, x=FAKE, M=4, N=64, K=256, w=FAKE, s=FAKE, aux=None, f=INT4, G=128, z=0, bias=None, act=0,
+         out=FAKE, od=0, ws=None, wsb=0):
+    return L.qlinear_forward(x, M, N, K, w, s, aux, f, G, z, bias, act, out, od, ws, wsb, None)
+
+
+def test_forward_validation_before_launch(L):
+    assert _fwd(L, M=0) == QL_OK                         # no-op
+    assert _fwd(L, x=None) == QL_E_ARG
+    assert _fwd(L, out=None) == QL_E_ARG
+    assert _fwd(L, x=FAKE + 8) == QL_E_ALIGN             # x must be 16-byte aligned
+    assert _fwd(L, out=FAKE + 1) == QL_E_ALIGN
+    assert _fwd(L, act=5) == QL_E_ARG
+    assert _fwd(L, od=3) == QL_E_ARG
+    assert _fwd(L, M=-1) == QL_E_SHAPE
+    assert _fwd(L, f=CB4, G=0, aux=None) == QL_E_ARG     # codebook record required
+    assert _fwd(L, z=1, aux=None) == QL_E_ARG            # zero-points required
+    # the 4096 x 4096 decode shape at M = 16 needs a split-K workspace
+    need = ctypes.c_size_t()
+    assert L.qlinear_workspace_bytes(INT4, 16, 4096, 4096, 128, 0, ctypes.byref(need)) == QL_OK
+    assert need.value > 0 and need.value % 256 == 0
+    assert _fwd(L, M=16, N=4096, K=4096, ws=None, wsb=0) == QL_E_WORKSPACE
+    assert _fwd(L, M=16, N=4096, K=4096, ws=FAKE, wsb=need.value - 1) == QL_E_WORKSPACE
+
+
+def test_workspace_bytes_is_a_pure_function(L):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    for M in (1, 4, 8, 16, 64, 128, 2048):
+        assert L.qlinear_workspace_bytes(INT8, M, 8192, 28672, 256, 1, ctypes.byref(a)) == QL_OK
+        assert L.qlinear_workspace_bytes(INT8, M, 8192, 28672, 256, 1, ctypes.byref(b)) == QL_OK
+        assert a.value == b.value
+    assert L.qlinear_workspace_bytes(INT8, 0, 8192, 28672, 256, 0, ctypes.byref(a)) == QL_OK and a.value == 0
+
+
+def test_pack_validation_before_launch(L):
+    half = np.linspace(0.1, 2.0, 8).astype(np.float32)
+    cent = np.concatenate([-half[::-1], half]).astype(np.float32)    # symmetric
+    asym = cent.copy()
+    asym[3] += 0.01
+    assert L.qlinear_pack(CB4, 64, 256, 0, FAKE, FAKE, asym.ctypes.data, FAKE, FAKE, FAKE, None) == QL_E_UNSUPPORTED
+    bad = cent.copy()
+    bad[0] = np.inf
+    assert L.qlinear_pack(CB4, 64, 256, 0, FAKE, FAKE, bad.ctypes.data, FAKE, FAKE, FAKE, None) == QL_E_UNSUPPORTED
+    assert L.qlinear_pack(CB4, 64, 256, 0, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == QL_E_ARG
+    assert L.qlinear_pack(INT8, 64, 256, 256, FAKE + 4, FAKE, None, FAKE, FAKE, None, None) == QL_E_ALIGN
+    assert L.qlinear_pack(INT4, 64, 256, 128, FAKE, FAKE, None, FAKE + 8, FAKE, None, None) == QL_E_ALIGN
+    assert L.qlinear_pack(MXFP4, 64, 256, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == QL_E_ARG
+    assert L.qlinear_pack(INT4, 64, 256, 128, None, FAKE, None, FAKE, FAKE, None, None) == QL_E_ARG
+
+
+def test_dequant_tile_validation(L):
+    assert L.qlinear_dequant_tile(INT4, 64, 256, 128, 0, FAKE, FAKE, None, 60, 0, 8, 8, 0, FAKE, None) == QL_E_SHAPE
+    assert L.qlinear_dequant_tile(INT4, 64, 256, 128, 0, FAKE, FAKE, None, 0, 0, 8, 8, 2, FAKE, None) == QL_E_ARG
+    assert L.qlinear_dequant_tile(INT4, 64, 256, 128, 0, FAKE, FAKE, None, 0, 0, 0, 8, 0, FAKE, None) == QL_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import bit_weight_only_offline_amd as Q
+    u8 = torch.zeros(256, dtype=torch.uint8)
+    pw = Q.PackedWeight(Q.QL_INT4, 64, 256, 128, 0, u8, u8, None)
+    with pytest.raises(Q.QLinearError, match="HIP device"):
+        Q.linear(torch.zeros((1, 256), dtype=torch.bfloat16), pw)
+    with pytest.raises(Q.QLinearError, match="grad"):
+        Q.linear(torch.zeros((1, 256), dtype=torch.bfloat16, requires_grad=True), pw)
