@@ -91,17 +91,17 @@ def _pool(Q, fmt, N, K, G, sym, seed, pool_bytes):
     return pool
 
 
-def time_forward(Q, pool, x, act, steps, warmup, use_graph=True):
+def time_forward(Q, pool, x, act, steps, warmup, use_graph=True, schedule=None):
     """Average time (ms) of one forward over `steps` forwards, each on the next pool copy."""
     import torch
     pw0 = pool[0]
     M = x.shape[0]
     out = torch.empty((M, pw0.N), dtype=torch.bfloat16, device=x.device)
-    wsb = Q.workspace_bytes(pw0.fmt, M, pw0.N, pw0.K, pw0.group, act)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
+    wsb = Q.workspace_bytes(pw0.fmt, M, pw0.N, pw0.K, pw0.group, act, schedule)
+    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=x.device)   # counters start at zero
 
     def run(i):
-        Q.linear(x, pool[i % len(pool)], act=act, out=out, workspace=ws)
+        Q.linear(x, pool[i % len(pool)], act=act, out=out, workspace=ws, schedule=schedule)
 
     for i in range(warmup):
         run(i)

@@ -17,6 +17,7 @@ import torch
 __all__ = [
     "QL_INT4", "QL_MXFP4", "QL_INT8", "QL_CB4", "FORMATS", "QLinearError", "lib", "version",
     "PackedWeight", "packed_bytes", "pack", "unpack", "dequant_tile", "workspace_bytes", "linear",
+    "Schedule", "default_schedule", "tile_shapes", "workspace",
 ]
 
 QL_INT4, QL_MXFP4, QL_INT8, QL_CB4 = 0, 1, 2, 3
@@ -28,6 +29,14 @@ _lib = None
 
 class QLinearError(RuntimeError):
     """A non-zero ql_status from the library."""
+
+
+class Schedule(ctypes.Structure):
+    """ql_schedule: tile = compiled tile shape (-1 automatic), splits = k-splits (0 automatic)."""
+    _fields_ = [("tile", ctypes.c_int32), ("splits", ctypes.c_int32)]
+
+    def __repr__(self) -> str:
+        return f"Schedule(tile={self.tile}, splits={self.splits})"
 
 
 def lib() -> ctypes.CDLL:
@@ -54,6 +63,17 @@ def lib() -> ctypes.CDLL:
         L.qlinear_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ci, ctypes.POINTER(sz)]
         L.qlinear_forward.restype = ci
         L.qlinear_forward.argtypes = [vp, i64, i64, i64, vp, vp, vp, ci, ci, ci, vp, ci, vp, ci, vp, sz, vp]
+        L.qlinear_num_tiles.restype = ci
+        L.qlinear_tile_shape.restype = ci
+        L.qlinear_tile_shape.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(ci)]
+        L.qlinear_default_schedule.restype = ci
+        L.qlinear_default_schedule.argtypes = [ci, i64, i64, i64, ci, ci, ctypes.POINTER(Schedule)]
+        L.qlinear_workspace_bytes_ex.restype = ci
+        L.qlinear_workspace_bytes_ex.argtypes = [ci, i64, i64, i64, ci, ci, ctypes.POINTER(Schedule),
+                                                 ctypes.POINTER(sz)]
+        L.qlinear_forward_ex.restype = ci
+        L.qlinear_forward_ex.argtypes = [vp, i64, i64, i64, vp, vp, vp, ci, ci, ci, vp, ci, vp, ci, vp, sz,
+                                         ctypes.POINTER(Schedule), vp]
         _lib = L
     return _lib
 
@@ -181,19 +201,63 @@ def dequant_tile(pw: PackedWeight, n0: int = 0, k0: int = 0, tn: int | None = No
     return out
 
 
-def workspace_bytes(fmt, M: int, N: int, K: int, group: int, act=None) -> int:
+def _sched(schedule):
+    if schedule is None:
+        return None
+    if isinstance(schedule, Schedule):
+        return ctypes.byref(schedule)
+    tile, splits = schedule
+    return ctypes.byref(Schedule(int(tile), int(splits)))
+
+
+def workspace_bytes(fmt, M: int, N: int, K: int, group: int, act=None, schedule=None) -> int:
     b = ctypes.c_size_t()
-    _check(lib().qlinear_workspace_bytes(_fmt(fmt), M, N, K, group, _ACT[act], ctypes.byref(b)),
-           "qlinear_workspace_bytes")
+    _check(lib().qlinear_workspace_bytes_ex(_fmt(fmt), M, N, K, group, _ACT[act], _sched(schedule),
+                                            ctypes.byref(b)), "qlinear_workspace_bytes")
     return b.value
+
+
+def default_schedule(fmt, M: int, N: int, K: int, group: int, act=None) -> Schedule:
+    s = Schedule()
+    _check(lib().qlinear_default_schedule(_fmt(fmt), M, N, K, group, _ACT[act], ctypes.byref(s)),
+           "qlinear_default_schedule")
+    return s
+
+
+def tile_shapes():
+    """[(rows, cols, kblock)] of the compiled tile shapes, by tile index."""
+    out = []
+    for t in range(lib().qlinear_num_tiles()):
+        r, c, k = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _check(lib().qlinear_tile_shape(t, ctypes.byref(r), ctypes.byref(c), ctypes.byref(k)), "qlinear_tile_shape")
+        out.append((r.value, c.value, k.value))
+    return out
+
+
+_WS = {}
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised workspace of at least nbytes on device, reused across calls
+    (the library leaves its arrival counters at zero after every call)."""
+    d = torch.device(device)
+    key = (d.type, d.index if d.index is not None else torch.cuda.current_device())
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=d)
+        _WS[key] = ws
+    return ws
 
 
 def linear(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, act=None,
            out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
-           workspace: torch.Tensor | None = None) -> torch.Tensor:
+           workspace: torch.Tensor | None = None, schedule=None) -> torch.Tensor:
     """Y = A . D(Wq)^T + b for bf16 x [..., K] (or [..., 2K] = [up | gate] with act="swiglu").
 
-    Inference only: inputs that require grad are rejected."""
+    workspace: a zero-initialised uint8 device buffer that stays owned by the caller and
+    may be reused (a shared one per device is used when omitted).  schedule: (tile,
+    splits) or a Schedule to override the automatic choice.  Inference only: inputs that
+    require grad are rejected."""
     if x.requires_grad or (bias is not None and bias.requires_grad):
         raise QLinearError("inference-only operator: inputs must not require grad")
     if x.device.type != "cuda" or pw.w.device.type != "cuda":
@@ -215,11 +279,17 @@ def linear(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, 
         raise QLinearError("out_dtype must be bfloat16 or float32")
     if out is None:
         out = torch.empty((M, pw.N), dtype=out_dtype, device=x.device)
-    ws_need = workspace_bytes(pw.fmt, M, pw.N, pw.K, pw.group, act)
-    if ws_need and (workspace is None or workspace.numel() < ws_need):
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=x.device)
-    _check(lib().qlinear_forward(_ptr(x2), M, pw.N, pw.K, _ptr(pw.w), _ptr(pw.s), _ptr(pw.aux), pw.fmt, pw.group,
-                                 pw.has_zeros, _ptr(bias), act_id, _ptr(out), 1 if out_dtype == torch.float32 else 0,
-                                 _ptr(workspace) if ws_need else None, ws_need, _stream(x.device)),
-           "qlinear_forward")
+    elif out.dtype != out_dtype or out.numel() != M * pw.N or not out.is_contiguous() or out.device != x.device:
+        raise QLinearError("out must be a contiguous [M, N] tensor of out_dtype on x's device")
+    ws_need = workspace_bytes(pw.fmt, M, pw.N, pw.K, pw.group, act, schedule)
+    if ws_need:
+        if workspace is None:
+            workspace = globals()["workspace"](x.device, ws_need)
+        elif workspace.numel() < ws_need or workspace.device != x.device:
+            raise QLinearError(f"workspace needs {ws_need} bytes on {x.device}")
+    _check(lib().qlinear_forward_ex(_ptr(x2), M, pw.N, pw.K, _ptr(pw.w), _ptr(pw.s), _ptr(pw.aux), pw.fmt,
+                                    pw.group, pw.has_zeros, _ptr(bias), act_id, _ptr(out),
+                                    1 if out_dtype == torch.float32 else 0,
+                                    _ptr(workspace) if ws_need else None, ws_need if ws_need else 0,
+                                    _sched(schedule), _stream(x.device)), "qlinear_forward")
     return out.reshape(*lead, pw.N)

@@ -24,6 +24,7 @@ SOURCES = [
     "ql_gemm_int8.hip",
     "ql_gemm_mxfp4.hip",
     "ql_gemm_cb4.hip",
+    "ql_misc.hip",
 ]
 
 ARCH = "gfx950"

@@ -15,32 +15,6 @@ namespace ql {
 // the MI355X / MI350X (gfx950), so workspace sizes can be queried without a device.
 constexpr int PLAN_CUS = 256;
 
-namespace {
-
-// Split-K reduction in a fixed order (s = 0, 1, ...), then the epilogue.
-__global__ void __launch_bounds__(256) qreduce_kernel(GemmArgs a) {
-    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= int64_t(a.M) * a.N) return;
-    const int m = int(idx / a.N), n = int(idx % a.N);
-    float v = 0.0f;
-    for (int s = 0; s < a.ks; ++s) v += a.ws[(int64_t(s) * a.M + m) * a.Np + n];
-    if (a.aux) {
-        // codebook (aux is only passed for CB4): row scale times 1/alpha
-        v *= reinterpret_cast<const float *>(a.s)[n] * reinterpret_cast<const CbRecord *>(a.aux)->inv_alpha;
-    }
-    if (a.bias) v += bf16_bits_to_f32(a.bias[n]);
-    if (a.out_f32) reinterpret_cast<float *>(a.out)[idx] = v;
-    else reinterpret_cast<__bf16 *>(a.out)[idx] = (__bf16)v;
-}
-
-}  // namespace
-
-hipError_t launch_reduce(const Layout &, const Plan &, const GemmArgs &a, hipStream_t st) {
-    const int64_t n = int64_t(a.M) * a.N;
-    hipLaunchKernelGGL(qreduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
 }  // namespace ql
 
 using namespace ql;
@@ -161,8 +135,60 @@ ql_status qlinear_dequant_tile(ql_format f, int64_t N, int64_t K, int group, int
                                         (hipStream_t)stream));
 }
 
-ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, int group, ql_act act,
-                                  size_t *bytes) {
+int qlinear_num_tiles(void) { return NUM_TILE_CFGS; }
+
+ql_status qlinear_tile_shape(int tile, int *rows, int *cols, int *kblock) {
+    if (tile < 0 || tile >= NUM_TILE_CFGS || !rows || !cols || !kblock) return QL_E_ARG;
+    const TileCfg &t = TILE_CFGS[tile];
+    *rows = 16 * t.MT;
+    *cols = (t.kind == 0 ? 16 : 64) * t.NT;
+    *kblock = t.SK;   // 0 for decode schedules (no activation staging)
+    return QL_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Resolve a (possibly partial) schedule into a launch plan.
+ql_status plan_for(ql_format f, int64_t M, int64_t N, int64_t K, int group, int has_zeros, ql_act act,
+                   const ql_schedule *sched, Layout *L, Plan *p) {
+    *L = layout_of(f, N, K, group, has_zeros);
+    int cfg = default_cfg(*L, M);
+    int splits = 0;
+    if (sched) {
+        if (sched->tile >= NUM_TILE_CFGS || sched->tile < -1) return QL_E_ARG;
+        if (sched->tile >= 0) cfg = sched->tile;
+        splits = sched->splits;
+        if (splits < 0) return QL_E_ARG;
+    }
+    if (is_decode(cfg) && (M > 16 || splits > 1)) return QL_E_UNSUPPORTED;   // decode: M <= 16, no split
+    *p = make_plan(*L, M, cfg, splits, PLAN_CUS, act == QL_ACT_SWIGLU);
+    return QL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ql_status qlinear_default_schedule(ql_format f, int64_t M, int64_t N, int64_t K, int group, ql_act act,
+                                   ql_schedule *out) {
+    if (!out) return QL_E_ARG;
+    if (act != QL_ACT_NONE && act != QL_ACT_SWIGLU) return QL_E_ARG;
+    if (M <= 0 || M >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    ql_status st = check_format(f, N, K, group, 0);
+    if (st != QL_OK) return st;
+    Layout L;
+    Plan p;
+    st = plan_for(f, M, N, K, group, 0, act, nullptr, &L, &p);
+    if (st != QL_OK) return st;
+    out->tile = p.cfg;
+    out->splits = p.ks;
+    return QL_OK;
+}
+
+ql_status qlinear_workspace_bytes_ex(ql_format f, int64_t M, int64_t N, int64_t K, int group, ql_act act,
+                                     const ql_schedule *sched, size_t *bytes) {
     if (!bytes) return QL_E_ARG;
     if (act != QL_ACT_NONE && act != QL_ACT_SWIGLU) return QL_E_ARG;
     if (M < 0 || M >= (int64_t(1) << 31)) return QL_E_SHAPE;
@@ -172,21 +198,31 @@ ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, 
         *bytes = 0;
         return QL_OK;
     }
-    const Layout L = layout_of(f, N, K, group, 0);
-    *bytes = make_plan(L, M, PLAN_CUS).ws_bytes;
+    Layout L;
+    Plan p;
+    st = plan_for(f, M, N, K, group, 0, act, sched, &L, &p);
+    if (st != QL_OK) return st;
+    *bytes = p.ws_bytes;
     return QL_OK;
 }
 
-ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K, const void *packed_w, const void *packed_s,
-                          const void *packed_aux, ql_format f, int group, int has_zeros, const void *bias, ql_act act,
-                          void *out, ql_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, int group, ql_act act,
+                                  size_t *bytes) {
+    return qlinear_workspace_bytes_ex(f, M, N, K, group, act, nullptr, bytes);
+}
+
+ql_status qlinear_forward_ex(const void *x, int64_t M, int64_t N, int64_t K, const void *packed_w,
+                             const void *packed_s, const void *packed_aux, ql_format f, int group, int has_zeros,
+                             const void *bias, ql_act act, void *out, ql_dtype out_dtype, void *workspace,
+                             size_t workspace_bytes, const ql_schedule *sched, void *stream) {
     ql_status st = check_format(f, N, K, group, has_zeros);
     if (st != QL_OK) return st;
     if (act != QL_ACT_NONE && act != QL_ACT_SWIGLU) return QL_E_ARG;
     if (out_dtype != QL_BF16 && out_dtype != QL_F32) return QL_E_ARG;
     if (M < 0 || M >= (int64_t(1) << 31)) return QL_E_SHAPE;
     const int64_t ldx = act == QL_ACT_SWIGLU ? 2 * K : K;
-    if (M * ldx >= (int64_t(1) << 31) || M * N >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    // activations are addressed with 32-bit buffer offsets whose bit 31 marks "out of range"
+    if (M * ldx >= (int64_t(1) << 30) || M * N >= (int64_t(1) << 31)) return QL_E_SHAPE;
     if (M == 0) return QL_OK;
     if (!x || !packed_w || !packed_s || !out) return QL_E_ARG;
     if (((f == QL_CB4) || (f == QL_INT4 && has_zeros)) && !packed_aux) return QL_E_ARG;
@@ -194,12 +230,15 @@ ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K, const 
     if (packed_aux && !aligned(packed_aux, 16)) return QL_E_ALIGN;
     if (bias && !aligned(bias, 2)) return QL_E_ALIGN;
     if (!aligned(out, out_dtype == QL_F32 ? 4 : 2)) return QL_E_ALIGN;
-    const Layout L = layout_of(f, N, K, group, has_zeros);
-    const Plan p = make_plan(L, M, PLAN_CUS);
+    Layout L;
+    Plan p;
+    st = plan_for(f, M, N, K, group, has_zeros, act, sched, &L, &p);
+    if (st != QL_OK) return st;
     if (p.ws_bytes > 0) {
         if (!workspace || workspace_bytes < p.ws_bytes) return QL_E_WORKSPACE;
-        if (!aligned(workspace, 16)) return QL_E_ALIGN;
+        if (!aligned(workspace, 256)) return QL_E_ALIGN;
     }
+    const bool decode = is_decode(p.cfg);
     GemmArgs a;
     a.x = static_cast<const uint16_t *>(x);
     a.w = static_cast<const uint8_t *>(packed_w);
@@ -208,7 +247,7 @@ ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K, const 
     a.aux = (f == QL_CB4) ? static_cast<const uint8_t *>(packed_aux) : nullptr;
     a.bias = static_cast<const uint16_t *>(bias);
     a.out = out;
-    a.ws = static_cast<float *>(workspace);
+    a.ws = (!decode && p.ks > 1) ? reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + p.ws_h) : nullptr;
     a.M = int(M);
     a.N = int(N);
     a.K = int(K);
@@ -219,13 +258,22 @@ ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K, const 
     a.ngroups = int(L.ngroups);
     a.cps = p.cps;
     a.ks = p.ks;
-    a.swiglu = act == QL_ACT_SWIGLU ? 1 : 0;
+    a.swiglu = (act == QL_ACT_SWIGLU && p.fuse_swiglu) ? 1 : 0;
     a.out_f32 = out_dtype == QL_F32 ? 1 : 0;
     a.w_bytes = uint32_t(L.w_bytes);
     a.s_bytes = uint32_t(L.s_bytes);
     a.z_bytes = uint32_t(L.aux_bytes);
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (act == QL_ACT_SWIGLU && !p.fuse_swiglu) {
+        // materialise h = bf16(up * silu(gate)) once, at the head of the workspace
+        uint16_t *h = static_cast<uint16_t *>(workspace);
+        e = launch_swiglu(a.x, h, a.M, a.K, s);
+        if (e != hipSuccess) return QL_E_HIP;
+        a.x = h;
+        a.ldx = a.K;
+        a.swiglu = 0;
+    }
     switch (f) {
         case QL_INT4: e = launch_gemm_int4(L, p, a, s); break;
         case QL_INT8: e = launch_gemm_int8(L, p, a, s); break;
@@ -233,8 +281,15 @@ ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K, const 
         default: e = launch_gemm_cb4(L, p, a, s); break;
     }
     if (e != hipSuccess) return QL_E_HIP;
-    if (p.ks > 1) e = launch_reduce(L, p, a, s);
+    if (!decode && p.ks > 1) e = launch_reduce(a, s);
     return from_hip(e);
+}
+
+ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K, const void *packed_w, const void *packed_s,
+                          const void *packed_aux, ql_format f, int group, int has_zeros, const void *bias, ql_act act,
+                          void *out, ql_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return qlinear_forward_ex(x, M, N, K, packed_w, packed_s, packed_aux, f, group, has_zeros, bias, act, out,
+                              out_dtype, workspace, workspace_bytes, nullptr, stream);
 }
 
 }  // extern "C"

@@ -81,10 +81,10 @@ struct GemmArgs {
     const uint8_t *w;      // packed tiles
     const uint8_t *s;      // packed scales
     const uint8_t *z;      // packed zero-points (INT4 with zeros)
-    const uint8_t *aux;    // codebook record (CB4)
+    const uint8_t *aux;    // codebook record (CB4 only, else null)
     const uint16_t *bias;  // bf16 [N] or null
     void *out;             // [M, N] bf16 or float32
-    float *ws;             // split-K partials [ks][M][Np]
+    float *ws;             // split-K partial sums [ks][M][Np]
     int M, N, K, ldx, Np;
     int ntiles, kchunks, ngroups;
     int cps, ks;           // chunks per split, number of splits
@@ -92,51 +92,87 @@ struct GemmArgs {
     uint32_t w_bytes, s_bytes, z_bytes;
 };
 
-// Tile shapes compiled for the linear kernel: MT m-tiles of 16 rows and NT column
-// tiles of 16 per wavefront, PF chunks of weights in flight per wavefront.
-struct TileCfg { int MT, NT, PF; };
-constexpr int NUM_TILE_CFGS = 5;
+// Schedules compiled into the library.
+//   kind 0 (decode, M <= 16): one workgroup per 16*NT output columns over the whole
+//           input dimension, split over WK wavefronts and reduced in LDS;
+//   kind 1 (tiles): 4 wavefronts side by side cover 16*MT rows x 64*NT columns, the
+//           activations staged through LDS in blocks of SK inputs; the input
+//           dimension may be split over workgroups (then a reduce kernel adds the
+//           partial sums in split order).
+// PF = weight chunks in flight per wavefront.
+struct TileCfg { int kind, MT, NT, SK, PF, WK; };
+constexpr int NUM_TILE_CFGS = 8;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
-    {1, 1, 8}, {1, 2, 4}, {2, 2, 4}, {4, 2, 4}, {8, 2, 2},
+    {0, 1, 1, 0, 4, 8}, {0, 1, 2, 0, 4, 8}, {0, 1, 4, 0, 4, 4}, {0, 1, 1, 0, 8, 4},
+    {1, 2, 2, 512, 4, 4}, {1, 4, 2, 256, 4, 4}, {1, 8, 2, 128, 2, 4}, {1, 8, 1, 128, 4, 4},
 };
 
 struct Plan {
     int cfg = 0;          // index into TILE_CFGS
     int mtiles = 1, nblocks = 1, ks = 1, cps = 1;
-    size_t ws_bytes = 0;
+    bool fuse_swiglu = false;   // SwiGLU formed while staging activations (tile kind)
+    size_t ws_h = 0;            // bytes of the materialised SwiGLU input at offset 0
+    size_t ws_bytes = 0;        // ws_h + split-K partial sums
 };
 
-// Chosen by M (rows), the column-tile count and the chunk count: enough workgroups to
-// cover every compute unit a few times, split-K only when the columns alone do not.
-inline Plan make_plan(const Layout &L, int64_t M, int num_cu) {
+// A tile workgroup recomputes silu for its own rows and input range, so fused SwiGLU
+// costs (column blocks) x M x K evaluations; beyond a couple of column blocks one
+// prologue pass that materialises h is cheaper.
+constexpr int FUSE_SWIGLU_MAX_NBLOCKS = 2;
+
+inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
+
+inline int default_cfg(const Layout &L, int64_t M) {
+    if (M <= 16) {
+        if (L.ntiles >= 1024) return 2;       // wide: four column tiles per wavefront
+        if (L.ntiles >= 512) return 1;
+        return 0;
+    }
+    if (M <= 32) return 4;
+    if (M <= 64) return 5;
+    return 6;
+}
+
+// splits <= 0 picks the split count automatically (tile schedules only): enough
+// workgroups to give every compute unit one, split-K only when the column blocks alone
+// do not, each split holding whole activation blocks and whole groups.
+inline Plan make_plan(const Layout &L, int64_t M, int cfg, int splits, int num_cu, bool swiglu) {
     Plan p;
-    if (M <= 16)
-        p.cfg = (L.ntiles >= 512) ? 1 : 0;
-    else if (M <= 32)
-        p.cfg = 2;
-    else if (M <= 64)
-        p.cfg = 3;
-    else
-        p.cfg = 4;
-    const TileCfg t = TILE_CFGS[p.cfg];
+    p.cfg = cfg;
+    const TileCfg t = TILE_CFGS[cfg];
+    const int ch = chunk_k(L.fmt);
+    int64_t span = 1;
+    if ((L.fmt == FMT_INT4 || L.fmt == FMT_INT8) && L.group > ch) span = L.group / ch;
+    if (t.kind == 0) {
+        // decode: the wavefronts of a workgroup split the chunks; cps = chunks per wavefront
+        p.mtiles = 1;
+        p.nblocks = int(ceil_div(L.ntiles, t.NT));
+        int64_t cpw = ceil_div(L.kchunks, t.WK);
+        cpw = ceil_div(cpw, span) * span;
+        p.cps = int(cpw);
+        p.ks = 1;
+        if (swiglu) p.ws_h = round256(size_t(M) * size_t(L.K) * 2);
+        p.ws_bytes = p.ws_h;
+        return p;
+    }
     p.mtiles = int(ceil_div(M, 16 * t.MT));
     p.nblocks = int(ceil_div(L.ntiles, 4 * t.NT));
     const int64_t wgs = int64_t(p.mtiles) * p.nblocks;
-    const int64_t target = 2 * int64_t(num_cu);
-    int64_t ks = 1;
-    if (wgs < target) ks = ceil_div(target, wgs);
-    // a split keeps at least two chunks and whole groups
-    int64_t span = 1;
-    if ((L.fmt == FMT_INT4 || L.fmt == FMT_INT8) && L.group > chunk_k(L.fmt))
-        span = L.group / chunk_k(L.fmt);
-    const int64_t max_ks = std::max<int64_t>(1, L.kchunks / std::max<int64_t>(2, span));
-    if (ks > max_ks) ks = max_ks;
+    int64_t ks = splits;
+    if (ks <= 0) {
+        ks = wgs < num_cu ? ceil_div(num_cu, wgs) : 1;
+        const int64_t blk = std::max<int64_t>(span, t.SK / ch);
+        ks = std::min<int64_t>(ks, std::max<int64_t>(1, L.kchunks / blk));
+    }
+    ks = std::max<int64_t>(1, std::min<int64_t>(ks, L.kchunks));
     int64_t cps = ceil_div(L.kchunks, ks);
     cps = ceil_div(cps, span) * span;
     ks = ceil_div(L.kchunks, cps);
     p.ks = int(ks);
     p.cps = int(cps);
-    p.ws_bytes = ks > 1 ? round256(size_t(ks) * size_t(M) * size_t(L.Np) * 4) : 0;
+    p.fuse_swiglu = swiglu && p.nblocks <= FUSE_SWIGLU_MAX_NBLOCKS;
+    if (swiglu && !p.fuse_swiglu) p.ws_h = round256(size_t(M) * size_t(L.K) * 2);
+    p.ws_bytes = p.ws_h + (ks > 1 ? round256(size_t(ks) * size_t(M) * size_t(L.Np) * 4) : 0);
     return p;
 }
 

@@ -2,20 +2,39 @@
 #pragma once
 
 #include "ql_gemm.hpp"
+#include "ql_gemv.hpp"
 
 namespace ql {
 
-template <int FMT, bool ZP, int GS>
-hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
-    const dim3 grid(p.nblocks, p.mtiles, p.ks), block(WG_THREADS);
-    switch (p.cfg) {
-        case 0: hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, 1, 1, 8>), grid, block, 0, st, a); break;
-        case 1: hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, 1, 2, 4>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, 2, 2, 4>), grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, 4, 2, 4>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, 8, 2, 2>), grid, block, 0, st, a); break;
+template <int FMT, bool ZP, int GS, int I>
+hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
+    constexpr TileCfg t = TILE_CFGS[I];
+    if constexpr (t.kind == 0) {
+        hipLaunchKernelGGL((qgemv_kernel<FMT, ZP, GS, t.NT, t.WK, t.PF>), dim3(p.nblocks), dim3(64 * t.WK), 0, st, a);
+    } else {
+        const dim3 grid(p.nblocks, p.mtiles, p.ks);
+        if (p.fuse_swiglu)
+            hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, t.MT, t.NT, t.SK, t.PF, true>), grid, dim3(WG_THREADS), 0, st, a);
+        else
+            hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, t.MT, t.NT, t.SK, t.PF, false>), grid, dim3(WG_THREADS), 0, st, a);
     }
     return hipGetLastError();
+}
+
+template <int FMT, bool ZP, int GS>
+hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
+    static_assert(NUM_TILE_CFGS == 8, "one case per compiled schedule");
+    switch (p.cfg) {
+        case 0: return launch_one<FMT, ZP, GS, 0>(p, a, st);
+        case 1: return launch_one<FMT, ZP, GS, 1>(p, a, st);
+        case 2: return launch_one<FMT, ZP, GS, 2>(p, a, st);
+        case 3: return launch_one<FMT, ZP, GS, 3>(p, a, st);
+        case 4: return launch_one<FMT, ZP, GS, 4>(p, a, st);
+        case 5: return launch_one<FMT, ZP, GS, 5>(p, a, st);
+        case 6: return launch_one<FMT, ZP, GS, 6>(p, a, st);
+        case 7: return launch_one<FMT, ZP, GS, 7>(p, a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int FMT, bool ZP>

@@ -19,6 +19,7 @@ hipError_t launch_gemm_int4(const Layout &L, const Plan &p, const GemmArgs &a, h
 hipError_t launch_gemm_int8(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_cb4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
-hipError_t launch_reduce(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
+hipError_t launch_reduce(const GemmArgs &a, hipStream_t st);
+hipError_t launch_swiglu(const uint16_t *x, uint16_t *h, int M, int K, hipStream_t st);
 
 }  // namespace ql

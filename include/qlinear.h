@@ -139,30 +139,77 @@ ql_status qlinear_dequant_tile(ql_format f, int64_t N, int64_t K, int group, int
                                float *out, void *stream);
 
 /*
- * Workspace that qlinear_forward() needs for this shape (split-K partial sums);
- * 0 when the chosen schedule reduces inside the kernel.  Host-only.
+ * Workspace that qlinear_forward() needs for this shape; 0 when no split of the input
+ * dimension over workgroups is scheduled.  Host-only (the schedule is a pure function
+ * of the shape, fixed for the 256 compute units of gfx950).
+ *
+ * The workspace holds float32 split-K partial sums (tile schedules) or the bf16 SwiGLU
+ * input h (decode schedules with act = SWIGLU).  Its contents on entry do not matter
+ * and are overwritten; calls that run at the same time must not share one.
  */
 ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, int group,
                                   ql_act act, size_t *bytes);
 
 /*
  * The linear layer.
- *   x          bf16 [M, K] (act = NONE) or [M, 2K] = [up | gate] (act = SWIGLU), row-major
- *   M          rows (0 is a no-op); N, K, group as packed
- *   packed_w, packed_s, packed_aux   from qlinear_pack() (packed_aux NULL for INT4
- *              symmetric, INT8 and MXFP4)
+ *   x          bf16 [M, K] (act = NONE) or [M, 2K] = [up | gate] (act = SWIGLU), row-major,
+ *              16-byte aligned
+ *   M          rows (0 is a no-op); N, K, group, has_zeros as packed
+ *   packed_w, packed_s, packed_aux   from qlinear_pack() (packed_aux may be NULL for INT4
+ *              without zero-points, INT8 and MXFP4)
  *   bias       bf16 [N] or NULL
- *   out        [M, N] row-major, bf16 (RNE of the float32 result) or float32
- *   workspace  device buffer of at least qlinear_workspace_bytes() (may be NULL if 0)
- * The path is chosen by M: a split-K streaming schedule for decode-sized M and an
- * LDS-staged matrix-core tile schedule for larger M; both accumulate in float32 and
- * reduce split-K partials in a fixed order, so results are run-to-run identical.
+ *   out        [M, N] row-major, bf16 (round to nearest even of the float32 result) or
+ *              float32 (the same float32 result)
+ *   workspace  at least qlinear_workspace_bytes() bytes, 256-byte aligned (NULL if 0)
+ * Schedules: for M <= 16 one workgroup per block of output columns streams the whole
+ * input dimension, split over its wavefronts and reduced in LDS; larger M uses tiles of
+ * 32 to 128 rows with activations staged through LDS, split over workgroups when the
+ * column blocks alone do not fill the device.  Both accumulate in float32 and add
+ * partial sums in a fixed order, so repeated calls give bit-identical results.
  */
 ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K,
                           const void *packed_w, const void *packed_s, const void *packed_aux,
                           ql_format f, int group, int has_zeros,
                           const void *bias, ql_act act, void *out, ql_dtype out_dtype,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Explicit schedules, for tuning.  CDNA kernels are sensitive to tile shapes (Petit
+ * package description, "Known limitations"), so the schedule that qlinear_forward()
+ * picks can be inspected and overridden.
+ *   tile    index of a compiled tile shape, 0 .. qlinear_num_tiles()-1, or -1 = automatic
+ *   splits  tile schedules: number of workgroups along the input dimension, or 0 =
+ *           automatic (rounded so that every split holds whole groups).  Decode
+ *           schedules split the input dimension over the wavefronts of one workgroup
+ *           and take splits 0 or 1; they serve M <= 16 only (QL_E_UNSUPPORTED
+ *           otherwise)
+ */
+typedef struct ql_schedule {
+    int32_t tile;
+    int32_t splits;
+} ql_schedule;
+
+/* Number of compiled schedules, and for each the rows x columns of output of one
+ * workgroup and the activation block it stages per barrier (0 for decode schedules,
+ * which read activations straight into registers). */
+int qlinear_num_tiles(void);
+ql_status qlinear_tile_shape(int tile, int *rows, int *cols, int *kblock);
+
+/* The schedule qlinear_forward() uses for a shape (host-only). */
+ql_status qlinear_default_schedule(ql_format f, int64_t M, int64_t N, int64_t K, int group,
+                                   ql_act act, ql_schedule *out);
+
+/* Workspace bytes for an explicit schedule (NULL = automatic). */
+ql_status qlinear_workspace_bytes_ex(ql_format f, int64_t M, int64_t N, int64_t K, int group,
+                                     ql_act act, const ql_schedule *sched, size_t *bytes);
+
+/* qlinear_forward() with an explicit schedule (NULL = automatic). */
+ql_status qlinear_forward_ex(const void *x, int64_t M, int64_t N, int64_t K,
+                             const void *packed_w, const void *packed_s, const void *packed_aux,
+                             ql_format f, int group, int has_zeros,
+                             const void *bias, ql_act act, void *out, ql_dtype out_dtype,
+                             void *workspace, size_t workspace_bytes, const ql_schedule *sched,
+                             void *stream);
 
 #ifdef __cplusplus
 }
