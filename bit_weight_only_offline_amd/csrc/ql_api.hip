@@ -140,9 +140,9 @@ int qlinear_num_tiles(void) { return NUM_TILE_CFGS; }
 ql_status qlinear_tile_shape(int tile, int *rows, int *cols, int *kblock) {
     if (tile < 0 || tile >= NUM_TILE_CFGS || !rows || !cols || !kblock) return QL_E_ARG;
     const TileCfg &t = TILE_CFGS[tile];
-    *rows = 16 * t.MT;
-    *cols = (t.kind == 0 ? 16 : 64) * t.NT;
-    *kblock = t.SK;   // 0 for decode schedules (no activation staging)
+    *rows = cfg_rows(t);
+    *cols = 16 * cfg_ntiles(t);
+    *kblock = t.kind == 0 ? 0 : (t.kind == 1 ? t.SK : 128);   // 0: no activation staging
     return QL_OK;
 }
 

@@ -99,13 +99,27 @@ struct GemmArgs {
 //           activations staged through LDS in blocks of SK inputs; the input
 //           dimension may be split over workgroups (then a reduce kernel adds the
 //           partial sums in split order).
-// PF = weight chunks in flight per wavefront.
-struct TileCfg { int kind, MT, NT, SK, PF, WK; };
-constexpr int NUM_TILE_CFGS = 8;
+//   kind 2 (LDS ring): WM x WN wavefronts, each 16*MT rows x 16*NT columns; activations
+//           and packed weights staged chunk by chunk into a PF-deep LDS ring by direct
+//           buffer->LDS loads (ql_gemm_lds.hpp); split-K as for kind 1.
+// PF = weight chunks in flight per wavefront (kinds 0, 1) or ring depth (kind 2).
+struct TileCfg { int kind, MT, NT, SK, PF, WK, WM, WN; };
+constexpr int NUM_TILE_CFGS = 13;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
-    {0, 1, 1, 0, 4, 8}, {0, 1, 2, 0, 4, 8}, {0, 1, 4, 0, 4, 4}, {0, 1, 1, 0, 8, 4},
-    {1, 2, 2, 512, 4, 4}, {1, 4, 2, 256, 4, 4}, {1, 8, 2, 128, 2, 4}, {1, 8, 1, 128, 4, 4},
+    {0, 1, 1, 0, 4, 8, 1, 1}, {0, 1, 2, 0, 4, 8, 1, 1}, {0, 1, 4, 0, 4, 4, 1, 1}, {0, 1, 1, 0, 8, 4, 1, 1},
+    {1, 2, 2, 512, 4, 4, 1, 4}, {1, 4, 2, 256, 4, 4, 1, 4}, {1, 8, 2, 128, 2, 4, 1, 4}, {1, 8, 1, 128, 4, 4, 1, 4},
+    {2, 8, 3, 0, 3, 4, 1, 4}, {2, 8, 4, 0, 3, 4, 1, 4}, {2, 4, 4, 0, 3, 4, 2, 2}, {2, 4, 3, 0, 4, 4, 1, 4},
+    {2, 2, 4, 0, 4, 4, 1, 4},
 };
+
+// Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.
+__host__ __device__ constexpr int cfg_rows(const TileCfg &t) { return 16 * t.MT * (t.kind == 2 ? t.WM : 1); }
+__host__ __device__ constexpr int cfg_ntiles(const TileCfg &t) {
+    return t.kind == 0 ? t.NT : (t.kind == 1 ? 4 * t.NT : t.NT * t.WN);
+}
+inline size_t lds_ring_bytes(const TileCfg &t, int fmt) {
+    return size_t(t.PF) * (size_t(cfg_rows(t)) * chunk_k(fmt) * 2 + size_t(cfg_ntiles(t)) * TILE_BYTES);
+}
 
 struct Plan {
     int cfg = 0;          // index into TILE_CFGS
@@ -130,7 +144,7 @@ inline int default_cfg(const Layout &L, int64_t M) {
     }
     if (M <= 32) return 4;
     if (M <= 64) return 5;
-    return 6;
+    return 8;
 }
 
 // splits <= 0 picks the split count automatically (tile schedules only): enough
@@ -155,13 +169,13 @@ inline Plan make_plan(const Layout &L, int64_t M, int cfg, int splits, int num_c
         p.ws_bytes = p.ws_h;
         return p;
     }
-    p.mtiles = int(ceil_div(M, 16 * t.MT));
-    p.nblocks = int(ceil_div(L.ntiles, 4 * t.NT));
+    p.mtiles = int(ceil_div(M, cfg_rows(t)));
+    p.nblocks = int(ceil_div(L.ntiles, cfg_ntiles(t)));
     const int64_t wgs = int64_t(p.mtiles) * p.nblocks;
     int64_t ks = splits;
     if (ks <= 0) {
         ks = wgs < num_cu ? ceil_div(num_cu, wgs) : 1;
-        const int64_t blk = std::max<int64_t>(span, t.SK / ch);
+        const int64_t blk = std::max<int64_t>(span, t.kind == 1 ? t.SK / ch : 2);
         ks = std::min<int64_t>(ks, std::max<int64_t>(1, L.kchunks / blk));
     }
     ks = std::max<int64_t>(1, std::min<int64_t>(ks, L.kchunks));
@@ -170,7 +184,7 @@ inline Plan make_plan(const Layout &L, int64_t M, int cfg, int splits, int num_c
     ks = ceil_div(L.kchunks, cps);
     p.ks = int(ks);
     p.cps = int(cps);
-    p.fuse_swiglu = swiglu && p.nblocks <= FUSE_SWIGLU_MAX_NBLOCKS;
+    p.fuse_swiglu = swiglu && t.kind == 1 && p.nblocks <= FUSE_SWIGLU_MAX_NBLOCKS;
     if (swiglu && !p.fuse_swiglu) p.ws_h = round256(size_t(M) * size_t(L.K) * 2);
     p.ws_bytes = p.ws_h + (ks > 1 ? round256(size_t(ks) * size_t(M) * size_t(L.Np) * 4) : 0);
     return p;

@@ -3,6 +3,7 @@
 
 #include "ql_gemm.hpp"
 #include "ql_gemv.hpp"
+#include "ql_gemm_lds.hpp"
 
 namespace ql {
 
@@ -11,6 +12,16 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
     constexpr TileCfg t = TILE_CFGS[I];
     if constexpr (t.kind == 0) {
         hipLaunchKernelGGL((qgemv_kernel<FMT, ZP, GS, t.NT, t.WK, t.PF>), dim3(p.nblocks), dim3(64 * t.WK), 0, st, a);
+    } else if constexpr (t.kind == 2) {
+        auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.MT, t.NT, t.PF>;
+        const size_t lds = lds_ring_bytes(t, FMT);
+        static bool attr_set = false;   // the dynamic-LDS limit is raised once per kernel
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        hipLaunchKernelGGL(kern, dim3(p.mtiles * p.nblocks, p.ks), dim3(64 * t.WM * t.WN), lds, st, a);
     } else {
         const dim3 grid(p.nblocks, p.mtiles, p.ks);
         if (p.fuse_swiglu)
@@ -23,7 +34,7 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
 
 template <int FMT, bool ZP, int GS>
 hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
-    static_assert(NUM_TILE_CFGS == 8, "one case per compiled schedule");
+    static_assert(NUM_TILE_CFGS == 13, "one case per compiled schedule");
     switch (p.cfg) {
         case 0: return launch_one<FMT, ZP, GS, 0>(p, a, st);
         case 1: return launch_one<FMT, ZP, GS, 1>(p, a, st);
@@ -33,6 +44,11 @@ hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
         case 5: return launch_one<FMT, ZP, GS, 5>(p, a, st);
         case 6: return launch_one<FMT, ZP, GS, 6>(p, a, st);
         case 7: return launch_one<FMT, ZP, GS, 7>(p, a, st);
+        case 8: return launch_one<FMT, ZP, GS, 8>(p, a, st);
+        case 9: return launch_one<FMT, ZP, GS, 9>(p, a, st);
+        case 10: return launch_one<FMT, ZP, GS, 10>(p, a, st);
+        case 11: return launch_one<FMT, ZP, GS, 11>(p, a, st);
+        case 12: return launch_one<FMT, ZP, GS, 12>(p, a, st);
         default: return hipErrorInvalidValue;
     }
 }
