@@ -36,6 +36,15 @@ __device__ inline void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier for the ring.  __syncthreads() carries a workgroup release fence,
+// and with LDS written by buffer loads that fence waits for EVERY outstanding load of
+// the wavefront (vmcnt(0)): the stages issued ahead would be drained at each chunk.
+// Here each wavefront has already waited for exactly the loads the barrier publishes;
+// its own LDS reads are waited for (lgkmcnt(0)) so the buffer the barrier frees is no
+// longer being read, and the "memory" clobber keeps the compiler from moving LDS
+// accesses or loads across it.
+__device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int FMT, bool ZP, int GS, int WM, int WN, int MTW, int NTW, int S>
 __global__ void __launch_bounds__(64 * WM * WN) qgemm_lds_kernel(GemmArgs a) {
     constexpr int W = WM * WN;
@@ -222,7 +231,7 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_lds_kernel(GemmArgs a) {
                 if (later >= 2) wait_vmcnt<2 * PER_STAGE>();
                 else if (later == 1) wait_vmcnt<PER_STAGE>();
                 else wait_vmcnt<0>();
-                __syncthreads();
+                ring_barrier();
                 if (i + S - 1 < nck) issue(i + S - 1, (u + S - 1) % S, sreg[(u + S - 1) % S], zreg[(u + S - 1) % S]);
                 compute(i, u, sreg[u], zreg[u]);
             }
