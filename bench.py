@@ -9,18 +9,27 @@ weights come from HBM.  Steps run back to back inside a HIP graph (the launch-bo
 inner loop), timed with HIP events on the stream the kernels run on.
 
 Also reported, on the same line:
-  sweep    the decode workload at M = 1, 4, 8, 16
   prefill  the 4-bit codebook workload at M = 2048 (3072 x 3072): TFLOP/s and the
            fraction of the dense bf16 matrix-core peak
-  roofline the dominant kernel against the HBM peak (8 TB/s)
+  roofline the decode kernel (the only kernel of the step) against the HBM peak
+           (8 TB/s), with the HBM traffic its FETCH_SIZE / WRITE_SIZE counters read
+           (calibrated on a plain copy), when recorded for the current kernel source
   cpu_baseline  the CPU oracle (dequantise, then a float64 product) on a bounded
            sample of the same workload, on the host cores
+  sweep    (--sweep) the decode workload at M = 1, 4, 8 and the other workloads
 
-Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--all]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--sweep]
+Profiling helpers (used to write the summaries kept with the benchmark):
+  python bench.py --probe              copy calibration + 20 decode dispatches, no timing
+  python bench.py --summarize-trace D  per-kernel durations from a rocprofv3 CSV trace
+  python bench.py --summarize-pmc F W  traffic per dispatch from FETCH_SIZE / WRITE_SIZE runs
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +43,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 POOL_BYTES = 1 << 30           # > 2 x the 256 MB Infinity Cache
+COPY_BYTES = 256 << 20         # calibration copy for the traffic counters
+
+# sources that define the decode kernel the roofline reports on; a recorded traffic
+# figure is used only while their hash is the one it was measured with
+KERNEL_SOURCES = ["ql_gemv.hpp", "ql_decode.hpp", "ql_common.hpp", "ql_gemm_dispatch.hpp", "ql_gemm_int4.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qgemv_int4_asym_decode_m16.txt")
+DECODE_KERNEL = "qgemv_kernel<0, true, 4"     # prefix of the INT4 zero-point g128 instantiation
 
 
 def alg_bytes(fmt, M, N, K, G, zeros, swiglu=False, bias=False):
@@ -89,6 +105,84 @@ def _pool(Q, fmt, N, K, G, sym, seed, pool_bytes):
                                    None if pw.aux is None else pw.aux.clone()))
     torch.cuda.synchronize()
     return pool
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_weight_only_offline_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch recorded in the counter summary, or None when the
+    summary is missing or was measured on another version of the kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    if kv.get("source_sha256", "").strip() != kernel_source_hash():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
+def _rows(pattern):
+    out = []
+    for f in sorted(glob.glob(pattern, recursive=True)):
+        with open(f, newline="") as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def summarize_trace(d):
+    """Per-kernel dispatch count and duration (µs) from a rocprofv3 --kernel-trace CSV."""
+    rows = _rows(os.path.join(d, "**", "*kernel_trace.csv"))
+    agg = {}
+    for r in rows:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        agg.setdefault(r["Kernel_Name"], []).append(dur)
+    lines = [f"{'calls':>6} {'avg_us':>9} {'median_us':>9} {'min_us':>8} {'max_us':>8}  kernel"]
+    for name, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        lines.append(f"{len(v):6d} {sum(v) / len(v):9.3f} {v[len(v) // 2]:9.3f} {v[0]:8.3f} {v[-1]:8.3f}  {name}")
+    return "\n".join(lines)
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Traffic of the decode kernel per dispatch from a FETCH_SIZE run and a WRITE_SIZE
+    run of `bench.py --probe`, each scaled by what the counter reads for the plain
+    device copy of COPY_BYTES in the same run."""
+    def per_kernel(d, counter):
+        agg = {}
+        for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
+            if r["Counter_Name"] == counter:
+                agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return agg
+
+    def pick(agg, key):
+        vals = [v for k, vs in agg.items() if key in k for v in vs]
+        return vals
+
+    out = {}
+    for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        agg = per_kernel(d, counter)
+        # the calibration copy: the dispatches that moved about COPY_BYTES
+        copies = [v for k, vs in agg.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs
+                  if v * 1024 > COPY_BYTES / 2]
+        kern = pick(agg, DECODE_KERNEL)
+        if not copies or not kern:
+            raise SystemExit(f"{counter}: calibration copy or decode kernel not found in {d}")
+        copy_kib = float(np.median(copies))
+        factor = (COPY_BYTES / 1024.0) / copy_kib
+        out[tag] = dict(copy_kib=copy_kib, factor=factor, kernel_kib=float(np.median(kern)), n=len(kern))
+    traffic = out["fetch"]["kernel_kib"] * 1024 * out["fetch"]["factor"] + \
+        out["write"]["kernel_kib"] * 1024 * out["write"]["factor"]
+    return out, int(round(traffic))
 
 
 def time_forward(Q, pool, x, act, steps, warmup, use_graph=True, schedule=None):
@@ -164,6 +258,32 @@ def cpu_baseline(wl_name, M, seconds=10.0):
                       f"{dt * 1e3:.1f} ms each"}
 
 
+def probe():
+    """Counter-collection workload: a plain device copy of COPY_BYTES (the calibration of
+    FETCH_SIZE / WRITE_SIZE) and 20 dispatches of the decode step; no timing."""
+    import torch
+
+    import bit_weight_only_offline_amd as Q
+    import synthetic as S
+    torch.cuda.set_device(0)
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    wl = S.WORKLOADS["int4_asym_decode"]
+    N, K, G = wl["N"], wl["K"], wl["group"]
+    pool = _pool(Q, "int4", N, K, G, False, 2, POOL_BYTES)
+    x = torch.from_numpy(S.activations(wl, 16)).cuda().to(torch.bfloat16)
+    out = torch.empty((16, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    for i in range(20):
+        Q.linear(x, pool[i % len(pool)], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"probe: copy {COPY_BYTES} bytes x3, decode M=16 x20 "
+          f"(kernel sources sha256 {kernel_source_hash()})", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,12 +291,29 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--all", action="store_true", help="also time every workload shape")
+    ap.add_argument("--sweep", action="store_true", help="also M = 1, 4, 8 and every other workload shape")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--probe", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_pmc:
+        parts, traffic = summarize_pmc(*args.summarize_pmc)
+        for tag, v in parts.items():
+            print(f"{tag}: copy_kib_per_dispatch: {v['copy_kib']:.1f} (copied {COPY_BYTES // 1024} KiB), "
+                  f"factor {v['factor']:.4f}; decode_kib_per_dispatch (median of {v['n']}): {v['kernel_kib']:.1f}")
+        print(f"source_sha256: {kernel_source_hash()}")
+        print(f"traffic_bytes_per_launch: {traffic}")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.probe:
+        probe()
+        return
 
     import torch
 
@@ -185,27 +322,29 @@ def main():
     torch.cuda.set_device(0)
     use_graph = not args.no_graph
 
+    # ---- the step: INT4 zero-point decode, M = 16 ----
     wl = S.WORKLOADS["int4_asym_decode"]
     N, K, G = wl["N"], wl["K"], wl["group"]
     pool = _pool(Q, "int4", N, K, G, False, 2, POOL_BYTES)
     n_copies = len(pool)
     xs = S.activations(wl, 16)
-    sweep = {}
-    main_ms = None
-    for M in (1, 4, 8, 16):
-        x = torch.from_numpy(xs[:M]).cuda().to(torch.bfloat16)
-        st = args.steps if M == 16 else max(50, args.steps // 2)
-        ms, _ = time_forward(Q, pool, x, None, st, args.warmup, use_graph)
-        b = alg_bytes("int4", M, N, K, G, True)
-        sweep[str(M)] = {"us": round(ms * 1e3, 3), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)}
-        if M == 16:
-            main_ms = ms
-    del pool
-    torch.cuda.empty_cache()
+    x16 = torch.from_numpy(xs[:16]).cuda().to(torch.bfloat16)
+    sched = Q.default_schedule("int4", 16, N, K, G)
+    main_ms, _ = time_forward(Q, pool, x16, None, args.steps, args.warmup, use_graph)
     b16 = alg_bytes("int4", 16, N, K, G, True)
     value = b16 / (main_ms * 1e-3) / 1e9
+    sweep = {}
+    if args.sweep:
+        for M in (1, 4, 8):
+            x = torch.from_numpy(xs[:M]).cuda().to(torch.bfloat16)
+            ms, _ = time_forward(Q, pool, x, None, max(50, args.steps // 2), args.warmup, use_graph)
+            b = alg_bytes("int4", M, N, K, G, True)
+            sweep[str(M)] = {"us": round(ms * 1e3, 3), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)}
+        sweep["16"] = {"us": round(main_ms * 1e3, 3), "GB/s": round(value, 1)}
+    del pool
+    torch.cuda.empty_cache()
 
-    # prefill: 4-bit codebook, 3072 x 3072, M = 2048
+    # ---- prefill: 4-bit codebook, 3072 x 3072, M = 2048 ----
     wl5 = S.WORKLOADS["cb4_prefill"]
     pool5 = _pool(Q, "cb4", wl5["N"], wl5["K"], 0, True, 5, 256 << 20)
     x5 = torch.from_numpy(S.activations(wl5, 2048)).cuda().to(torch.bfloat16)
@@ -213,12 +352,13 @@ def main():
     fl = 2.0 * 2048 * wl5["N"] * wl5["K"]
     tflops = fl / (ms5 * 1e-3) / 1e12
     prefill = {"workload": "cb4 Lloyd-Max codebook 3072x3072, M=2048, bf16", "us": round(ms5 * 1e3, 2),
-               "TFLOP/s": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+               "TFLOP/s": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+               "schedule": repr(Q.default_schedule("cb4", 2048, wl5["N"], wl5["K"], 0))}
     del pool5
     torch.cuda.empty_cache()
 
     others = {}
-    if args.all:
+    if args.sweep:
         for name, M_list in (("mxfp4_up", (1, 16, 64)), ("mxfp4_down", (1, 16, 64)), ("int8_swiglu", (1, 16, 128)),
                              ("cb4_prefill", (256,))):
             w_ = S.WORKLOADS[name]
@@ -251,13 +391,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "int4 asym g128 decode linear, W 4096x4096 (fp16 scales, 4-bit zeros), "
                                "X bf16 [16,4096], bf16 out", "M": 16, "N": N, "K": K, "group": G,
-                   "weight_pool_copies": n_copies, "hip_graph": use_graph},
+                   "weight_pool_copies": n_copies, "hip_graph": use_graph, "schedule": repr(sched)},
         "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
-        "sweep": sweep,
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                     "kernel": "qgemv_kernel (INT4, zero-points, group 128)", "alg_bytes": b16,
+                     "us_per_launch": round(main_ms * 1e3, 3)},
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
+    if sweep:
+        rec["sweep"] = sweep
     if others:
         rec["others"] = others
     print(json.dumps(rec), flush=True)
