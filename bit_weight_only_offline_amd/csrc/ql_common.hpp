@@ -117,6 +117,33 @@ __host__ __device__ constexpr int cfg_rows(const TileCfg &t) { return 16 * t.MT 
 __host__ __device__ constexpr int cfg_ntiles(const TileCfg &t) {
     return t.kind == 0 ? t.NT : (t.kind == 1 ? 4 * t.NT : t.NT * t.WN);
 }
+// One stage of a decode wavefront's LDS ring: NT packed weight tiles, the chunk's
+// scale words and zero-point words (256-byte blocks), then the activation block of 16
+// rows x one chunk of bf16.
+__host__ __device__ constexpr int gemv_spc(int fmt, int gs) {
+    return (fmt == FMT_INT4 || fmt == FMT_INT8) ? (gs <= chunk_k(fmt) / 32 ? chunk_k(fmt) / 32 / gs : 1) : 1;
+}
+__host__ __device__ constexpr int gemv_scale_blocks(int fmt, int gs, int nt) {
+    return (fmt == FMT_INT4 || fmt == FMT_INT8) ? (nt * gemv_spc(fmt, gs) * 8 + 63) / 64
+                                               : (fmt == FMT_MXFP4 ? (nt * 16 + 63) / 64 : 0);
+}
+__host__ __device__ constexpr int gemv_zero_blocks(int fmt, bool zp, int gs, int nt) {
+    return (fmt == FMT_INT4 && zp) ? (nt * gemv_spc(fmt, gs) * 2 + 63) / 64 : 0;
+}
+__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt) {
+    return nt * TILE_BYTES + 256 * (gemv_scale_blocks(fmt, gs, nt) + gemv_zero_blocks(fmt, zp, gs, nt)) +
+           16 * chunk_k(fmt) * 2;
+}
+constexpr int LDS_BYTES_MAX = 160 * 1024;
+// ring depth: PF stages per wavefront, fewer if they would not fit the LDS
+__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf) {
+    return pf * wk * gemv_stage_bytes(fmt, zp, gs, nt) <= LDS_BYTES_MAX
+               ? pf
+               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt));
+}
+__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf) {
+    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf) * gemv_stage_bytes(fmt, zp, gs, nt);
+}
 inline size_t lds_ring_bytes(const TileCfg &t, int fmt) {
     return size_t(t.PF) * (size_t(cfg_rows(t)) * chunk_k(fmt) * 2 + size_t(cfg_ntiles(t)) * TILE_BYTES);
 }

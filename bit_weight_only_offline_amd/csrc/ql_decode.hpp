@@ -45,6 +45,49 @@ __device__ inline uint32_t ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
+// Direct buffer -> LDS load of 16 bytes per lane: lane l's bytes land at lds + 16*l
+// (lds is wave-uniform).  Counted by vmcnt like any vector-memory load; out-of-range
+// offsets write zeros.
+__device__ inline void ld128_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wavefront are outstanding.  The
+// counter is 6 bits wide: a larger N is clamped to 63, which only waits longer.
+template <int N0>
+__device__ inline void wait_vmcnt() {
+    constexpr int N = N0 > 63 ? 63 : N0;
+    static_assert(N >= 0, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits 15:14; expcnt (6:4)
+    // and lgkmcnt (11:8) left at their maxima (no wait)
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Direct buffer -> LDS load of 4 bytes per lane: lane l's word lands at lds + 4*l.
+__device__ inline void ld32_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, off, 0, 0, 0);
+}
+
+// wait_vmcnt with a wave-uniform run-time count (a scalar jump over immediates).
+__device__ inline void wait_vmcnt_rt(int n) {
+#define QL_WAIT_CASE(k) \
+    case k: wait_vmcnt<k>(); break;
+#define QL_WAIT_CASE8(k) QL_WAIT_CASE(k) QL_WAIT_CASE(k + 1) QL_WAIT_CASE(k + 2) QL_WAIT_CASE(k + 3) \
+    QL_WAIT_CASE(k + 4) QL_WAIT_CASE(k + 5) QL_WAIT_CASE(k + 6) QL_WAIT_CASE(k + 7)
+    switch (n <= 0 ? 0 : n) {
+        QL_WAIT_CASE8(0) QL_WAIT_CASE8(8) QL_WAIT_CASE8(16) QL_WAIT_CASE8(24)
+        QL_WAIT_CASE8(32) QL_WAIT_CASE8(40) QL_WAIT_CASE8(48)
+        QL_WAIT_CASE(56) QL_WAIT_CASE(57) QL_WAIT_CASE(58) QL_WAIT_CASE(59) QL_WAIT_CASE(60) QL_WAIT_CASE(61)
+        QL_WAIT_CASE(62)
+        default: wait_vmcnt<63>(); break;
+    }
+#undef QL_WAIT_CASE8
+#undef QL_WAIT_CASE
+}
+
+// Compiler-only fence: no memory access moves across it (the hardware is not waited).
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
 __device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ inline float f16_bits_to_f32(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);

@@ -7,20 +7,31 @@
 
 namespace ql {
 
+// Raise a kernel's dynamic-LDS limit to `bytes`, once per kernel (the flag is per
+// instantiation of the caller).
+inline hipError_t allow_dynamic_lds(const void *kern, size_t bytes, bool &done) {
+    if (done) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
 template <int FMT, bool ZP, int GS, int I>
 hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
     constexpr TileCfg t = TILE_CFGS[I];
     if constexpr (t.kind == 0) {
-        hipLaunchKernelGGL((qgemv_kernel<FMT, ZP, GS, t.NT, t.WK, t.PF>), dim3(p.nblocks), dim3(64 * t.WK), 0, st, a);
+        auto kern = qgemv_kernel<FMT, ZP, GS, t.NT, t.WK, t.PF>;
+        constexpr size_t lds = gemv_lds_bytes(FMT, ZP, GS, t.NT, t.WK, t.PF);
+        static bool attr_set = false;
+        hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(64 * t.WK), lds, st, a);
     } else if constexpr (t.kind == 2) {
         auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.MT, t.NT, t.PF>;
         const size_t lds = lds_ring_bytes(t, FMT);
-        static bool attr_set = false;   // the dynamic-LDS limit is raised once per kernel
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        static bool attr_set = false;
+        hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(p.mtiles * p.nblocks, p.ks), dim3(64 * t.WM * t.WN), lds, st, a);
     } else {
         const dim3 grid(p.nblocks, p.mtiles, p.ks);

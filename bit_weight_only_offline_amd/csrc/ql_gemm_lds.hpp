@@ -25,17 +25,6 @@
 
 namespace ql {
 
-// Wait until at most N vector-memory loads of this wavefront are outstanding.  The
-// counter is 6 bits wide: a larger N is clamped to 63, which only waits longer.
-template <int N0>
-__device__ inline void wait_vmcnt() {
-    constexpr int N = N0 > 63 ? 63 : N0;
-    static_assert(N >= 0, "vmcnt range");
-    // gfx9 s_waitcnt: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits 15:14; expcnt (6:4)
-    // and lgkmcnt (11:8) left at their maxima (no wait)
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Workgroup barrier for the ring.  __syncthreads() carries a workgroup release fence,
 // and with LDS written by buffer loads that fence waits for EVERY outstanding load of
 // the wavefront (vmcnt(0)): the stages issued ahead would be drained at each chunk.
@@ -119,16 +108,13 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_lds_kernel(GemmArgs a) {
             const uint32_t bad = (uint32_t(~(int32_t(k - a.K) >> 31)) | uint32_t(~(int32_t(m - a.M) >> 31))) &
                                  0x80000000u;
             const uint32_t off = ((uint32_t(m) * uint32_t(a.ldx) + uint32_t(k)) * 2u) | bad;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (__attribute__((address_space(3))) void *)(base + j * 1024), 16, off, 0, 0, 0);
+            ld128_lds(xr, off, base + j * 1024);
         }
 #pragma unroll
         for (int q = 0; q < NB / W; ++q) {
             const int j = wv + W * q;
             const uint32_t tile = uint32_t(nt0 + j) * uint32_t(a.kchunks) + uint32_t(kc);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (__attribute__((address_space(3))) void *)(base + A_BYTES + j * 1024), 16,
-                tile * TILE_BYTES + lane * 16, 0, 0, 0);
+            ld128_lds(wr, tile * TILE_BYTES + lane * 16, base + A_BYTES + j * 1024);
         }
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {

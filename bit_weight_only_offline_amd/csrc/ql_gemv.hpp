@@ -2,13 +2,18 @@
 //
 // One workgroup owns NT column tiles (16*NT output columns) over the whole input
 // dimension; its WK wavefronts split the chunks of the input dimension into WK
-// contiguous runs (whole groups each).  Every wavefront streams its run of packed
-// weight tiles and the matching A fragments (the activation rows, read straight into
-// registers) PF chunks ahead, decodes the weights in registers and accumulates with
-// v_mfma_f32_16x16x32_bf16 (A rows beyond M are never loaded: their products only
-// reach output rows that are not stored).  At the end the WK partial tiles are added in
-// LDS in wavefront order -- a fixed order -- and the epilogue applies the codebook row
-// scale and the bias and rounds to bf16.  No workspace, no cross-workgroup traffic.
+// contiguous runs (whole groups each).  Every wavefront streams its run through a
+// private LDS ring, several chunks ahead, with direct buffer->LDS loads only: per chunk
+// the packed weight tiles, the scale and zero-point words and the activation block
+// (16 rows x one chunk of inputs).  The activation loads read whole rows of the chunk
+// (full 128-byte lines) and only the rows below M are requested; a XOR swizzle of the
+// 16-byte pieces makes each A-fragment read a conflict-free ds_read_b128.  Nothing is
+// loaded into registers, so every wait is explicit: a wavefront waits (vmcnt) only for
+// the chunk it is about to use.  Weights are decoded in registers and accumulated with
+// v_mfma_f32_16x16x32_bf16 (A rows at or beyond M never reach a stored output).  At the
+// end the WK partial tiles are added in LDS in wavefront order -- a fixed order -- and
+// the epilogue applies the codebook row scale and the bias and rounds to bf16.  No
+// workspace, no cross-workgroup traffic.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,13 +23,35 @@
 
 namespace ql {
 
+// Activation block of one chunk in LDS: 16 rows x chunk_k(FMT) bf16, as NI wave-wide
+// loads of 1 KiB.  A row of the chunk is P 16-byte pieces; one load covers RPI rows.
+// Piece p of row r sits at 16-byte slot (r % RPI) * P + (p ^ xswz(r)) of load r / RPI.
+template <int FMT>
+struct XBlock {
+    static constexpr int P = chunk_k(FMT) * 2 / 16;   // 16 (4-bit formats) or 8 (INT8)
+    static constexpr int RPI = 64 / P;                // rows per load
+    static constexpr int NI = 16 / RPI;               // loads per chunk
+    static constexpr int BYTES = NI * 1024;
+    // distinct low 4 bits of the slot for the 16 rows of one fragment read
+    __device__ static constexpr int xswz(int r) { return P == 16 ? (r & 15) : ((r >> 1) & 7); }
+};
+
 template <int FMT, bool ZP, int GS, int NT, int WK, int PF>
 __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int CH = chunk_k(FMT);
     constexpr int STEPS = CH / 32;
     constexpr bool INTF = (FMT == FMT_INT4 || FMT == FMT_INT8);
-    constexpr int SPC = INTF ? (GS <= STEPS ? STEPS / GS : 1) : 1;
-    __shared__ float red[WK][NT][4][64];
+    constexpr int SPC = gemv_spc(FMT, GS);
+    using XB = XBlock<FMT>;
+    constexpr int NSS = gemv_scale_blocks(FMT, GS, NT);
+    constexpr int NSZ = gemv_zero_blocks(FMT, ZP, GS, NT);
+    constexpr int S_OFF = NT * TILE_BYTES;
+    constexpr int Z_OFF = S_OFF + 256 * NSS;
+    constexpr int X_OFF = Z_OFF + 256 * NSZ;
+    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT);
+    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF);
+    static_assert(X_OFF + XB::BYTES == STAGE && S >= 1 && S <= 8, "stage layout");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // [WK][S][STAGE]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keep it scalar
@@ -33,15 +60,105 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     // this wavefront's run of chunks: cps per wavefront (a multiple of the group span)
     const int kc0 = wv * a.cps;
     const int nck = max(0, min(a.kchunks - kc0, a.cps));
+    uint8_t *ring = lds + wv * (S * STAGE);
 
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.s, a.s_bytes);
     const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z, ZP ? a.z_bytes : 0u);
+    // activations through a ranged buffer: rows >= M and inputs >= K read as zero
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint32_t(int64_t(a.M) * a.ldx * 2));
     const uint32_t s_shift = 16u * (c & 1);                       // this column's fp16/bf16 scale
     const uint32_t z_shift = 8u * ((c >> 1) & 3) + 4u * (c & 1);  // and its 4-bit zero-point
 
     CbLut lut = {0u, 0u, 0u, 0u};
     if (FMT == FMT_CB4) lut = reinterpret_cast<const CbRecord *>(a.aux)->lut;
+
+    // ---- per-lane parts of the loads ----
+    // activation loads actually issued: those holding a row below M (wave-uniform)
+    const int nia = min(XB::NI, (a.M + XB::RPI - 1) / XB::RPI);
+    uint32_t xrow[XB::NI];
+    int xk[XB::NI];
+#pragma unroll
+    for (int j = 0; j < XB::NI; ++j) {
+        const int r = j * XB::RPI + lane / XB::P;
+        const int pc = (lane % XB::P) ^ XB::xswz(r);
+        xrow[j] = (r < a.M) ? uint32_t(r) * uint32_t(a.ldx) * 2u : 0x80000000u;   // bit 31: not fetched
+        xk[j] = 8 * pc;
+    }
+    // this lane's A fragment of k-step t: row c, piece 4t + g
+    uint32_t xfrag[STEPS];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t)
+        xfrag[t] = uint32_t(X_OFF + (c / XB::RPI) * 1024 + ((c % XB::RPI) * XB::P + ((4 * t + g) ^ XB::xswz(c))) * 16);
+    // scale / zero-point words: word e of a chunk's scale block is word (e % 8) of the
+    // record of tile e / (8 SPC), group slot (e / 8) % SPC (MXFP4: column e % 16 of tile
+    // e / 16); zero-point words likewise with 2 words per record
+    int s_tile[NSS > 0 ? NSS : 1], s_q[NSS > 0 ? NSS : 1], s_w[NSS > 0 ? NSS : 1];
+#pragma unroll
+    for (int d = 0; d < NSS; ++d) {
+        const int e = d * 64 + lane;
+        if (FMT == FMT_MXFP4) {
+            s_tile[d] = e / 16;
+            s_q[d] = 0;
+            s_w[d] = e % 16;
+        } else {
+            s_tile[d] = e / (8 * SPC);
+            s_q[d] = (e / 8) % SPC;
+            s_w[d] = e % 8;
+        }
+    }
+    int z_tile[NSZ > 0 ? NSZ : 1], z_q[NSZ > 0 ? NSZ : 1], z_w[NSZ > 0 ? NSZ : 1];
+#pragma unroll
+    for (int d = 0; d < NSZ; ++d) {
+        const int e = d * 64 + lane;
+        z_tile[d] = e / (2 * SPC);
+        z_q[d] = (e / 2) % SPC;
+        z_w[d] = e % 2;
+    }
+    // the group record of group slot q in chunk kc
+    auto group_of = [&](int kc, int q) -> uint32_t {
+        return (GS <= STEPS) ? uint32_t(kc * (STEPS / GS) + q) : uint32_t(kc / (GS / STEPS));
+    };
+
+    // issue every load of chunk i (relative) into ring slot `slot`
+    auto issue = [&](int i, int slot) {
+        const int kc = kc0 + i;
+        uint8_t *base = ring + slot * STAGE;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const uint32_t tile = uint32_t(ntb + j) * uint32_t(a.kchunks) + uint32_t(kc);
+            ld128_lds(wr, tile * TILE_BYTES + lane * 16, base + j * TILE_BYTES);
+        }
+#pragma unroll
+        for (int d = 0; d < NSS; ++d) {
+            uint32_t off;
+            if (FMT == FMT_MXFP4) {
+                const uint32_t tile = uint32_t(ntb + s_tile[d]) * uint32_t(a.kchunks) + uint32_t(kc);
+                off = (tile * TILE_N + uint32_t(s_w[d])) * 4;
+            } else {
+                const uint32_t rec = uint32_t(ntb + s_tile[d]) * uint32_t(a.ngroups) + group_of(kc, s_q[d]);
+                off = rec * (TILE_N * 2) + uint32_t(s_w[d]) * 4;
+            }
+            if (s_tile[d] >= NT) off = 0x80000000u;                 // past this chunk's records
+            ld32_lds(sr, off, base + S_OFF + d * 256);
+        }
+#pragma unroll
+        for (int d = 0; d < NSZ; ++d) {
+            const uint32_t rec = uint32_t(ntb + z_tile[d]) * uint32_t(a.ngroups) + group_of(kc, z_q[d]);
+            uint32_t off = rec * 8 + uint32_t(z_w[d]) * 4;
+            if (z_tile[d] >= NT) off = 0x80000000u;
+            ld32_lds(zr, off, base + Z_OFF + d * 256);
+        }
+#pragma unroll
+        for (int j = 0; j < XB::NI; ++j) {
+            if (j < nia) {
+                const int k = kc * CH + xk[j];
+                const uint32_t past_k = uint32_t(~(int32_t(k - a.K) >> 31)) & 0x80000000u;   // k >= K
+                ld128_lds(xr, (xrow[j] + uint32_t(k) * 2u) | past_k, base + X_OFF + j * 1024);
+            }
+        }
+    };
+    const int per_chunk = NT + NSS + NSZ + nia;   // vector-memory loads issued per chunk
 
     f32x4 acc[NT], tmp[NT], xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -49,54 +166,33 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const u32x4 ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const bf16x8 ones = as_bf16x8(ones_u);
 
-    u32x4 wreg[PF][NT];
-    uint32_t sreg[PF][NT][SPC];
-    uint32_t zreg[PF][NT][SPC];
-    u32x4 xreg[PF][STEPS];
-    // activations through a ranged buffer: rows >= M and inputs >= K read as zero
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint32_t(int64_t(a.M) * a.ldx * 2));
-    // lanes of rows >= M read from an offset beyond the buffer (bit 31 set)
-    const uint32_t xrow = (c < a.M) ? uint32_t(c) * uint32_t(a.ldx) * 2u : 0x80000000u;
-
-    auto load_chunk = [&](int i, u32x4 (&wq)[NT], uint32_t (&sq)[NT][SPC], uint32_t (&zq)[NT][SPC],
-                          u32x4 (&xq)[STEPS]) {
+    auto compute = [&](int i, int slot) {
         const int kc = kc0 + i;
+        // chunk i has landed once only the chunks issued after it are outstanding
+        wait_vmcnt_rt(per_chunk * min(S - 1, nck - 1 - i));
+        compiler_fence();
+        const uint8_t *base = ring + slot * STAGE;
+        u32x4 wq[NT];
+        uint32_t sq[NT][SPC], zq[NT][SPC];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const uint32_t tile = uint32_t(ntb + j) * uint32_t(a.kchunks) + uint32_t(kc);
-            wq[j] = ld128(wr, tile * TILE_BYTES + lane * 16);
-            if (FMT == FMT_MXFP4) {
-                sq[j][0] = ld32(sr, (tile * TILE_N + c) * 4);
-            } else if (INTF) {
+            wq[j] = *reinterpret_cast<const u32x4 *>(base + j * TILE_BYTES + lane * 16);
 #pragma unroll
-                for (int q = 0; q < SPC; ++q) {
-                    const uint32_t grp = (GS <= STEPS) ? uint32_t(kc * (STEPS / GS) + q) : uint32_t(kc / (GS / STEPS));
-                    const uint32_t rec = uint32_t(ntb + j) * uint32_t(a.ngroups) + grp;
-                    // aligned 32-bit words; the lane's field is selected when it is used,
-                    // so no extension of a sub-dword load forces an early wait
-                    sq[j][q] = ld32(sr, ((rec * TILE_N + c) * 2) & ~3u);
-                    if (ZP) zq[j][q] = ld32(zr, (rec * 8 + (c >> 1)) & ~3u);
+            for (int q = 0; q < SPC; ++q) {
+                if (FMT == FMT_MXFP4) {
+                    sq[j][q] = *reinterpret_cast<const uint32_t *>(base + S_OFF + (j * 16 + c) * 4);
+                } else if (INTF) {
+                    sq[j][q] = *reinterpret_cast<const uint32_t *>(base + S_OFF + ((j * SPC + q) * 8 + (c >> 1)) * 4);
+                    if (ZP) zq[j][q] = *reinterpret_cast<const uint32_t *>(base + Z_OFF + ((j * SPC + q) * 2 + (c >> 3)) * 4);
                 }
             }
         }
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
-            const int k = kc * CH + 32 * t + 8 * g;
-            const uint32_t past_k = uint32_t(~(int32_t(k - a.K) >> 31)) & 0x80000000u;   // k >= K
-            xq[t] = ld128(xr, (xrow + uint32_t(k) * 2u) | past_k);
-        }
-    };
-
-    const u32x4 ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-    const bf16x8 ones = as_bf16x8(ones_u);
-
-    auto compute = [&](int i, const u32x4 (&wq)[NT], const uint32_t (&sq)[NT][SPC], const uint32_t (&zq)[NT][SPC],
-                       const u32x4 (&xq)[STEPS]) {
-        const int kc = kc0 + i;
-#pragma unroll
-        for (int t = 0; t < STEPS; ++t) {
-            const bf16x8 af = as_bf16x8(xq[t]);
+            const bf16x8 af = *reinterpret_cast<const bf16x8 *>(base + xfrag[t]);
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 u32x4 bw;
@@ -140,24 +236,30 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     };
 
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
-        if (u < nck) load_chunk(u, wreg[u], sreg[u], zreg[u], xreg[u]);
-    for (int i0 = 0; i0 < nck; i0 += PF) {
+    for (int u = 0; u < S; ++u)
+        if (u < nck) issue(u, u);
+    for (int i0 = 0; i0 < nck; i0 += S) {
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
+        for (int u = 0; u < S; ++u) {
             const int i = i0 + u;
             if (i < nck) {
-                compute(i, wreg[u], sreg[u], zreg[u], xreg[u]);
-                if (i + PF < nck) load_chunk(i + PF, wreg[u], sreg[u], zreg[u], xreg[u]);
+                compute(i, u);
+                if (i + S < nck) {
+                    // the slot is refilled: this wavefront's reads of it must be complete
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    issue(i + S, u);
+                }
             }
         }
     }
 
     // ---- wavefront reduction in LDS (fixed order), then the epilogue ----
+    __syncthreads();                      // every ring is drained: reuse the LDS
+    float *red = reinterpret_cast<float *>(lds);   // [WK][NT][4][64]
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wv][j][r][lane] = acc[j][r];
+        for (int r = 0; r < 4; ++r) red[((wv * NT + j) * 4 + r) * 64 + lane] = acc[j][r];
     __syncthreads();
     // output element e = (j, r, lane): row g*4 + r, column (ntb + j)*16 + c
     for (int e = tid; e < NT * 4 * 64; e += 64 * WK) {
@@ -166,7 +268,7 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
         if (m >= a.M || n >= a.N) continue;
         float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < WK; ++w) v += red[w][j][r][l];
+        for (int w = 0; w < WK; ++w) v += red[((w * NT + j) * 4 + r) * 64 + l];
         if (FMT == FMT_CB4) v *= reinterpret_cast<const float *>(a.s)[n] * reinterpret_cast<const CbRecord *>(a.aux)->inv_alpha;
         if (a.bias) v += bf16_bits_to_f32(a.bias[n]);
         if (a.out_f32) reinterpret_cast<float *>(a.out)[int64_t(m) * a.N + n] = v;
