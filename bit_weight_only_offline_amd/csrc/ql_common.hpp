@@ -99,17 +99,19 @@ struct GemmArgs {
 //           activations staged through LDS in blocks of SK inputs; the input
 //           dimension may be split over workgroups (then a reduce kernel adds the
 //           partial sums in split order).
-//   kind 2 (LDS ring): WM x WN wavefronts, each 16*MT rows x 16*NT columns; activations
+//   kind 2 (LDS ring): WM x WN wavefronts, each 16*MT rows x 16*NT columns, times WK
+//           wavefronts that share a tile and split each chunk's k-steps; activations
 //           and packed weights staged chunk by chunk into a PF-deep LDS ring by direct
 //           buffer->LDS loads (ql_gemm_lds.hpp); split-K as for kind 1.
 // PF = weight chunks in flight per wavefront (kinds 0, 1) or ring depth (kind 2).
 struct TileCfg { int kind, MT, NT, SK, PF, WK, WM, WN; };
-constexpr int NUM_TILE_CFGS = 13;
+constexpr int NUM_TILE_CFGS = 17;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {0, 1, 1, 0, 4, 8, 1, 1}, {0, 1, 2, 0, 4, 8, 1, 1}, {0, 1, 4, 0, 4, 4, 1, 1}, {0, 1, 1, 0, 8, 4, 1, 1},
     {1, 2, 2, 512, 4, 4, 1, 4}, {1, 4, 2, 256, 4, 4, 1, 4}, {1, 8, 2, 128, 2, 4, 1, 4}, {1, 8, 1, 128, 4, 4, 1, 4},
-    {2, 8, 3, 0, 3, 4, 1, 4}, {2, 8, 4, 0, 3, 4, 1, 4}, {2, 4, 4, 0, 3, 4, 2, 2}, {2, 4, 3, 0, 4, 4, 1, 4},
-    {2, 2, 4, 0, 4, 4, 1, 4},
+    {2, 8, 3, 0, 3, 1, 1, 4}, {2, 8, 4, 0, 3, 1, 1, 4}, {2, 4, 4, 0, 3, 1, 2, 2}, {2, 4, 3, 0, 4, 1, 1, 4},
+    {2, 2, 4, 0, 4, 1, 1, 4}, {2, 8, 3, 0, 3, 2, 1, 4}, {2, 8, 4, 0, 3, 2, 1, 4}, {2, 4, 4, 0, 4, 2, 1, 4},
+    {2, 4, 3, 0, 4, 2, 1, 4},
 };
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.
@@ -144,8 +146,25 @@ __host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int 
 __host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf) {
     return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf) * gemv_stage_bytes(fmt, zp, gs, nt);
 }
-inline size_t lds_ring_bytes(const TileCfg &t, int fmt) {
-    return size_t(t.PF) * (size_t(cfg_rows(t)) * chunk_k(fmt) * 2 + size_t(cfg_ntiles(t)) * TILE_BYTES);
+// LDS of a ring schedule: PF stages of activations + packed tiles + every wavefront's
+// scale and zero-point words, or, when WK > 1, the hand-over of one k-half's
+// accumulators if that is larger.
+__host__ __device__ constexpr int ring_stage_bytes(int fmt, bool zp, int gs, int wm, int wn, int wk, int mt, int nt) {
+    return 16 * mt * wm * chunk_k(fmt) * 2 + nt * wn * TILE_BYTES +
+           wm * wn * wk * 256 * (gemv_scale_blocks(fmt, gs, nt) + gemv_zero_blocks(fmt, zp, gs, nt));
+}
+// ring depth: PF stages, fewer if they would not fit the LDS
+__host__ __device__ constexpr int ring_depth(int fmt, bool zp, int gs, int wm, int wn, int wk, int mt, int nt, int pf) {
+    return pf * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt) <= LDS_BYTES_MAX
+               ? pf
+               : LDS_BYTES_MAX / ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt);
+}
+// pf: the ring depth actually used (ring_depth)
+__host__ __device__ constexpr int ring_lds_bytes(int fmt, bool zp, int gs, int wm, int wn, int wk, int mt, int nt,
+                                                 int pf) {
+    return pf * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt) > (wk > 1 ? wm * wn * mt * nt * 1024 : 0)
+               ? pf * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt)
+               : wm * wn * mt * nt * 1024;
 }
 
 struct Plan {
@@ -163,15 +182,23 @@ constexpr int FUSE_SWIGLU_MAX_NBLOCKS = 2;
 
 inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 
+// Default schedule by batch size (measured on MI355X over the workload shapes):
+//   M <= 16      decode kernel, more column tiles per wavefront for wide layers;
+//   M <= 64      32 x 256 ring tiles, split-K to fill the machine;
+//   M <= 256     64-row ring tiles, two wavefronts per tile (INT8: 256 columns);
+//   larger M     128 x 192 ring tiles, two wavefronts per tile (INT formats, whose
+//                group accumulators need the registers: one wavefront per tile).
 inline int default_cfg(const Layout &L, int64_t M) {
     if (M <= 16) {
         if (L.ntiles >= 1024) return 2;       // wide: four column tiles per wavefront
         if (L.ntiles >= 512) return 1;
         return 0;
     }
-    if (M <= 32) return 4;
-    if (M <= 64) return 5;
-    return 8;
+    if (M <= 64) return 12;
+    const bool intf = L.fmt == FMT_INT4 || L.fmt == FMT_INT8;
+    if (M <= 256) return L.fmt == FMT_INT8 ? 15 : 16;
+    if (L.fmt == FMT_INT8) return 16;
+    return intf ? 8 : 13;
 }
 
 // splits <= 0 picks the split count automatically (tile schedules only): enough
@@ -201,7 +228,9 @@ inline Plan make_plan(const Layout &L, int64_t M, int cfg, int splits, int num_c
     const int64_t wgs = int64_t(p.mtiles) * p.nblocks;
     int64_t ks = splits;
     if (ks <= 0) {
-        ks = wgs < num_cu ? ceil_div(num_cu, wgs) : 1;
+        // enough workgroups to give every compute unit one (a machine already three
+        // quarters full is not split: the split costs a reduce pass)
+        ks = 4 * wgs < 3 * int64_t(num_cu) ? ceil_div(num_cu, wgs) : 1;
         const int64_t blk = std::max<int64_t>(span, t.kind == 1 ? t.SK / ch : 2);
         ks = std::min<int64_t>(ks, std::max<int64_t>(1, L.kchunks / blk));
     }

@@ -27,12 +27,14 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(64 * t.WK), lds, st, a);
     } else if constexpr (t.kind == 2) {
-        auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.MT, t.NT, t.PF>;
-        const size_t lds = lds_ring_bytes(t, FMT);
+        constexpr int depth = ring_depth(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, t.PF);
+        auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth>;
+        constexpr size_t lds = ring_lds_bytes(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth);
+        static_assert(lds <= LDS_BYTES_MAX, "ring fits the LDS");
         static bool attr_set = false;
         hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(p.mtiles * p.nblocks, p.ks), dim3(64 * t.WM * t.WN), lds, st, a);
+        hipLaunchKernelGGL(kern, dim3(p.mtiles * p.nblocks, p.ks), dim3(64 * t.WM * t.WN * t.WK), lds, st, a);
     } else {
         const dim3 grid(p.nblocks, p.mtiles, p.ks);
         if (p.fuse_swiglu)
@@ -45,7 +47,7 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
 
 template <int FMT, bool ZP, int GS>
 hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
-    static_assert(NUM_TILE_CFGS == 13, "one case per compiled schedule");
+    static_assert(NUM_TILE_CFGS == 17, "one case per compiled schedule");
     switch (p.cfg) {
         case 0: return launch_one<FMT, ZP, GS, 0>(p, a, st);
         case 1: return launch_one<FMT, ZP, GS, 1>(p, a, st);
@@ -60,6 +62,10 @@ hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
         case 10: return launch_one<FMT, ZP, GS, 10>(p, a, st);
         case 11: return launch_one<FMT, ZP, GS, 11>(p, a, st);
         case 12: return launch_one<FMT, ZP, GS, 12>(p, a, st);
+        case 13: return launch_one<FMT, ZP, GS, 13>(p, a, st);
+        case 14: return launch_one<FMT, ZP, GS, 14>(p, a, st);
+        case 15: return launch_one<FMT, ZP, GS, 15>(p, a, st);
+        case 16: return launch_one<FMT, ZP, GS, 16>(p, a, st);
         default: return hipErrorInvalidValue;
     }
 }

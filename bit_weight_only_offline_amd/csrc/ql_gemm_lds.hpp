@@ -2,8 +2,11 @@
 // into an S-deep LDS ring by gfx950 direct buffer->LDS loads (buffer_load_dwordx4 ...
 // lds), so nothing is staged through registers and several chunks are in flight.
 //
-// Workgroup = WM x WN wavefronts; a wavefront owns 16*MTW rows x 16*NTW columns, so a
-// workgroup covers 16*MTW*WM rows and 16*NTW*WN columns.  One ring stage holds one chunk
+// Workgroup = WM x WN x WKK wavefronts; a wavefront owns 16*MTW rows x 16*NTW columns, so
+// a workgroup covers 16*MTW*WM rows and 16*NTW*WN columns.  With WKK = 2 two wavefronts
+// share each output tile and take alternate halves of every chunk's k-steps (two
+// wavefronts per SIMD hide each other's LDS and decode latency); their accumulators are
+// added in LDS, in a fixed order, before the epilogue.  One ring stage holds one chunk
 // of the input dimension (128 inputs, 64 for INT8):
 //   A  [k-step][8-wide slice][row] x 16 bytes: the A-fragment order, so each lane's
 //      fragment is one conflict-free ds_read_b128;
@@ -12,7 +15,9 @@
 // Per stage every wavefront waits for its own loads (s_waitcnt vmcnt), one barrier makes
 // all of them visible and frees the oldest buffer, the loads of the stage S-1 ahead are
 // issued, and the chunk is consumed: one ds_read_b128 per packed tile, register decode,
-// MTW x NTW MFMAs per k-step.  Scales ride in registers (S-deep ring).  Out-of-range
+// MTW x NTW MFMAs per k-step.  Each wavefront's scale and zero-point words of the chunk
+// ride in the same stage (4-byte direct loads), so every load of the loop goes to LDS
+// and every wait is explicit.  Out-of-range
 // rows and inputs load as zero (ranged buffer loads).  Workgroups are numbered so that
 // the ones sharing activation rows run on the same XCD (blocks are dealt round-robin to
 // the 8 XCDs, each with its own L2).
@@ -34,29 +39,41 @@ namespace ql {
 // accesses or loads across it.
 __device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int FMT, bool ZP, int GS, int WM, int WN, int MTW, int NTW, int S>
-__global__ void __launch_bounds__(64 * WM * WN) qgemm_lds_kernel(GemmArgs a) {
-    constexpr int W = WM * WN;
+template <int FMT, bool ZP, int GS, int WM, int WN, int WKK, int MTW, int NTW, int S>
+__global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs a) {
+    constexpr int W = WM * WN * WKK;
     constexpr int CH = chunk_k(FMT);
     constexpr int STEPS = CH / 32;
+    constexpr int SPW = STEPS / WKK;                // k-steps of a chunk per wavefront
+    static_assert(SPW * WKK == STEPS, "k-steps split evenly");
     constexpr bool INTF = (FMT == FMT_INT4 || FMT == FMT_INT8);
     constexpr int SPC = INTF ? (GS <= STEPS ? STEPS / GS : 1) : 1;
     constexpr int MP = 16 * MTW * WM;               // rows of the workgroup tile
     constexpr int NTT = NTW * WN;                   // column tiles of the workgroup
     constexpr int A_BYTES = MP * CH * 2;
     constexpr int B_BYTES = NTT * TILE_BYTES;
-    constexpr int STAGE = A_BYTES + B_BYTES;
+    // every wavefront's scale / zero-point words of its NTW tiles (256-byte blocks)
+    constexpr int NSS = gemv_scale_blocks(FMT, GS, NTW);
+    constexpr int NSZ = gemv_zero_blocks(FMT, ZP, GS, NTW);
+    constexpr int SCW = 256 * (NSS + NSZ);
+    constexpr int STAGE = A_BYTES + B_BYTES + W * SCW;
+    static_assert(STAGE == ring_stage_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW), "stage layout");
     constexpr int NA = A_BYTES / 1024;              // wave-wide A loads per stage
     constexpr int NB = NTT;                         // wave-wide B loads per stage
-    static_assert(NA % W == 0 && NB % W == 0, "loads must split evenly over the wavefronts");
-    constexpr int SL = INTF ? NTW * SPC * (ZP ? 2 : 1) : (FMT == FMT_MXFP4 ? NTW : 0);
-    constexpr int PER_STAGE = NA / W + NB / W + SL;  // vector-memory ops per wavefront per stage
+    static_assert(NA % W == 0, "activation loads split evenly over the wavefronts");
+
     static_assert(S >= 2 && S <= 4, "ring depth");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv / WN, wn = wv % WN;
+    const int kh = wv / (WM * WN);                  // which k-steps of each chunk
+    const int wm = (wv % (WM * WN)) / WN, wn = wv % WN;
+    // B tiles are dealt round-robin, every wavefront issuing NBW loads: tile (wv + W q) mod
+    // NB, so when W does not divide NB a few tiles are fetched twice (identical bytes to
+    // the same LDS slot) and every wavefront waits for the same count
+    constexpr int NBW = (NB + W - 1) / W;
+    constexpr int PER_STAGE = NA / W + NBW + NSS + NSZ;   // vector-memory loads per wavefront per stage
     const int g = lane >> 4, c = lane & 15;
 
     // XCD-aware numbering: block b runs on XCD b % 8; give each XCD a contiguous range of
@@ -92,60 +109,108 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_lds_kernel(GemmArgs a) {
             tmp[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    uint32_t sreg[S][NTW][SPC], zreg[S][NTW][SPC];
 
-    // issue the loads of chunk i (relative) into ring buffer buf, scales into slot buf
-    auto issue = [&](int i, int buf, uint32_t (&sq)[NTW][SPC], uint32_t (&zq)[NTW][SPC]) {
+    // per-lane parts of the ring loads that do not change from chunk to chunk: the
+    // activation slot's row (rows >= M get bit 31: never fetched) and input offset, and
+    // the weight tile's column block
+    uint32_t a_off[NA / W];
+    int a_k[NA / W];
+#pragma unroll
+    for (int q = 0; q < NA / W; ++q) {
+        const int sidx = (wv + W * q) * 64 + lane;        // 16-byte slot = (block, row)
+        const int row = sidx % MP, blk = sidx / MP;
+        const int m = m0 + row;
+        a_k[q] = 32 * (blk >> 2) + 8 * (blk & 3);
+        a_off[q] = (m < a.M) ? (uint32_t(m) * uint32_t(a.ldx) + uint32_t(a_k[q])) * 2u : 0x80000000u;
+    }
+    uint32_t b_off[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q)
+        b_off[q] = uint32_t(nt0 + (wv + W * q) % NB) * uint32_t(a.kchunks) * TILE_BYTES + uint32_t(lane) * 16u;
+
+    // scale / zero-point words: word e of this wavefront's scale block is word (e % 8) of
+    // the record of its tile e / (8 SPC), group slot (e / 8) % SPC (MXFP4: column e % 16
+    // of tile e / 16); zero-point words likewise with 2 words per record
+    int s_tile[NSS > 0 ? NSS : 1], s_q[NSS > 0 ? NSS : 1], s_w[NSS > 0 ? NSS : 1];
+#pragma unroll
+    for (int d = 0; d < NSS; ++d) {
+        const int e = d * 64 + lane;
+        s_tile[d] = (FMT == FMT_MXFP4) ? e / 16 : e / (8 * SPC);
+        s_q[d] = (FMT == FMT_MXFP4) ? 0 : (e / 8) % SPC;
+        s_w[d] = (FMT == FMT_MXFP4) ? e % 16 : e % 8;
+    }
+    int z_tile[NSZ > 0 ? NSZ : 1], z_q[NSZ > 0 ? NSZ : 1], z_w[NSZ > 0 ? NSZ : 1];
+#pragma unroll
+    for (int d = 0; d < NSZ; ++d) {
+        const int e = d * 64 + lane;
+        z_tile[d] = e / (2 * SPC);
+        z_q[d] = (e / 2) % SPC;
+        z_w[d] = e % 2;
+    }
+    auto group_of = [&](int kc, int q) -> uint32_t {
+        return (GS <= STEPS) ? uint32_t(kc * (STEPS / GS) + q) : uint32_t(kc / (GS / STEPS));
+    };
+
+    // issue the loads of chunk i (relative) into ring buffer buf
+    auto issue = [&](int i, int buf) {
         const int kc = kc0 + i;
         uint8_t *base = lds + buf * STAGE;
         const int kbase = kc * CH;
+        const bool whole = kbase + CH <= a.K;               // wave-uniform: no input past K
 #pragma unroll
         for (int q = 0; q < NA / W; ++q) {
-            const int j = wv + W * q;                        // which 1 KiB of the A stage
-            const int sidx = j * 64 + lane;                  // 16-byte slot = (block, row)
-            const int row = sidx % MP, blk = sidx / MP;
-            const int m = m0 + row, k = kbase + 32 * (blk >> 2) + 8 * (blk & 3);
-            const uint32_t bad = (uint32_t(~(int32_t(k - a.K) >> 31)) | uint32_t(~(int32_t(m - a.M) >> 31))) &
-                                 0x80000000u;
-            const uint32_t off = ((uint32_t(m) * uint32_t(a.ldx) + uint32_t(k)) * 2u) | bad;
-            ld128_lds(xr, off, base + j * 1024);
+            uint32_t off = a_off[q] + uint32_t(kbase) * 2u;
+            if (!whole && kbase + a_k[q] >= a.K) off |= 0x80000000u;
+            ld128_lds(xr, off, base + (wv + W * q) * 1024);
         }
 #pragma unroll
-        for (int q = 0; q < NB / W; ++q) {
-            const int j = wv + W * q;
-            const uint32_t tile = uint32_t(nt0 + j) * uint32_t(a.kchunks) + uint32_t(kc);
-            ld128_lds(wr, tile * TILE_BYTES + lane * 16, base + A_BYTES + j * 1024);
+        for (int q = 0; q < NBW; ++q)
+            ld128_lds(wr, b_off[q] + uint32_t(kc) * TILE_BYTES, base + A_BYTES + ((wv + W * q) % NB) * 1024);
+        uint8_t *sc = base + A_BYTES + B_BYTES + wv * SCW;
+#pragma unroll
+        for (int d = 0; d < NSS; ++d) {
+            const uint32_t ntg = uint32_t(nt0 + wn * NTW + s_tile[d]);
+            uint32_t off;
+            if (FMT == FMT_MXFP4) off = ((ntg * uint32_t(a.kchunks) + uint32_t(kc)) * TILE_N + uint32_t(s_w[d])) * 4;
+            else off = (ntg * uint32_t(a.ngroups) + group_of(kc, s_q[d])) * (TILE_N * 2) + uint32_t(s_w[d]) * 4;
+            if (s_tile[d] >= NTW) off = 0x80000000u;               // past this wavefront's records
+            ld32_lds(sr, off, sc + d * 256);
         }
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int ntg = nt0 + wn * NTW + j;
-            if (FMT == FMT_MXFP4) {
-                const uint32_t tile = uint32_t(ntg) * uint32_t(a.kchunks) + uint32_t(kc);
-                sq[j][0] = ld32(sr, (tile * TILE_N + c) * 4);
-            } else if (INTF) {
-#pragma unroll
-                for (int q = 0; q < SPC; ++q) {
-                    const uint32_t grp = (GS <= STEPS) ? uint32_t(kc * (STEPS / GS) + q) : uint32_t(kc / (GS / STEPS));
-                    const uint32_t rec = uint32_t(ntg) * uint32_t(a.ngroups) + grp;
-                    sq[j][q] = ld32(sr, ((rec * TILE_N + c) * 2) & ~3u);
-                    if (ZP) zq[j][q] = ld32(zr, (rec * 8 + (c >> 1)) & ~3u);
-                }
-            }
+        for (int d = 0; d < NSZ; ++d) {
+            const uint32_t ntg = uint32_t(nt0 + wn * NTW + z_tile[d]);
+            uint32_t off = (ntg * uint32_t(a.ngroups) + group_of(kc, z_q[d])) * 8 + uint32_t(z_w[d]) * 4;
+            if (z_tile[d] >= NTW) off = 0x80000000u;
+            ld32_lds(zr, off, sc + (NSS + d) * 256);
         }
     };
 
     const u32x4 ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const bf16x8 ones = as_bf16x8(ones_u);
 
-    auto compute = [&](int i, int buf, const uint32_t (&sq)[NTW][SPC], const uint32_t (&zq)[NTW][SPC]) {
+    auto compute = [&](int i, int buf) {
         const int kc = kc0 + i;
         const uint8_t *A = lds + buf * STAGE;
         const uint8_t *Bt = A + A_BYTES;
+        const uint8_t *sc = A + A_BYTES + B_BYTES + wv * SCW;
         u32x4 wq[NTW];
+        uint32_t sq[NTW][SPC], zq[NTW][SPC];
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) wq[j] = *reinterpret_cast<const u32x4 *>(Bt + (wn * NTW + j) * 1024 + lane * 16);
+        for (int j = 0; j < NTW; ++j) {
+            wq[j] = *reinterpret_cast<const u32x4 *>(Bt + (wn * NTW + j) * 1024 + lane * 16);
 #pragma unroll
-        for (int t = 0; t < STEPS; ++t) {
+            for (int q = 0; q < SPC; ++q) {
+                if (FMT == FMT_MXFP4) {
+                    sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + (j * 16 + c) * 4);
+                } else if (INTF) {
+                    sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + ((j * SPC + q) * 8 + (c >> 1)) * 4);
+                    if (ZP) zq[j][q] = *reinterpret_cast<const uint32_t *>(sc + NSS * 256 + ((j * SPC + q) * 2 + (c >> 3)) * 4);
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < SPW; ++tt) {
+            const int t = kh * SPW + tt;
             bf16x8 af[MTW];
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt)
@@ -167,9 +232,11 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_lds_kernel(GemmArgs a) {
             if (INTF) {
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt) xs[mt] = mfma16x16x32(af[mt], ones, xs[mt]);
+                // fold the partial group sums at the last of this wavefront's steps in
+                // the group (a group may span both halves of a chunk, or several chunks)
                 bool boundary;
-                if (GS <= STEPS) boundary = ((t + 1) % GS) == 0;
-                else boundary = (t == STEPS - 1) && (((kc + 1) % (GS / STEPS)) == 0);
+                if (GS <= STEPS) boundary = ((t + 1) % GS) == 0 || tt == SPW - 1;
+                else boundary = (tt == SPW - 1) && (((kc + 1) % (GS / STEPS)) == 0);
                 if (boundary) {
                     const int q = (GS <= STEPS) ? (t / GS) : 0;
 #pragma unroll
@@ -204,7 +271,7 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_lds_kernel(GemmArgs a) {
     // ---- prologue: stages 0 .. S-2 in flight ----
 #pragma unroll
     for (int u = 0; u < S - 1; ++u)
-        if (u < nck) issue(u, u, sreg[u], zreg[u]);
+        if (u < nck) issue(u, u);
 
     // ---- main loop, unrolled by the ring depth so ring slots are compile-time ----
     for (int i0 = 0; i0 < nck; i0 += S) {
@@ -218,10 +285,36 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_lds_kernel(GemmArgs a) {
                 else if (later == 1) wait_vmcnt<PER_STAGE>();
                 else wait_vmcnt<0>();
                 ring_barrier();
-                if (i + S - 1 < nck) issue(i + S - 1, (u + S - 1) % S, sreg[(u + S - 1) % S], zreg[(u + S - 1) % S]);
-                compute(i, u, sreg[u], zreg[u]);
+                if (i + S - 1 < nck) issue(i + S - 1, (u + S - 1) % S);
+                compute(i, u);
             }
         }
+    }
+
+    if constexpr (WKK > 1) {
+        // add the k-halves in a fixed order: the wavefronts of the second half hand their
+        // accumulators over through LDS (every ring is drained by now)
+        static_assert(WM * WN * MTW * NTW * 1024 <= ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S),
+                      "hand-over fits the allocation");
+        __syncthreads();
+        float *red = reinterpret_cast<float *>(lds);
+        const int slot = wv % (WM * WN);
+        if (kh == 1) {
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[(((slot * MTW + mt) * NTW + j) * 4 + r) * 64 + lane] = acc[mt][j][r];
+        }
+        __syncthreads();
+        if (kh != 0) return;
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[mt][j][r] += red[(((slot * MTW + mt) * NTW + j) * 4 + r) * 64 + lane];
     }
 
     // ---- epilogue ----

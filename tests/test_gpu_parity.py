@@ -220,6 +220,14 @@ def test_swiglu_fused_equals_materialised(fmt, G, M, N):
     torch.cuda.synchronize()
     assert rel_err(y_fused.cpu().numpy(), yref) <= TOL
     assert torch.equal(y_fused, y_dev_h)
+    if M > 16:
+        # the tile kernel forms h while staging the activations when few column blocks
+        # would recompute it: same result as that kernel on the materialised h
+        y_k1 = Q.linear(bf16_tensor(raw), pw, bf16_tensor(b), act="swiglu", out_dtype=torch.float32, schedule=(4, 0))
+        y_k1_h = Q.linear(hd, pw, bf16_tensor(b), out_dtype=torch.float32, schedule=(4, 0))
+        torch.cuda.synchronize()
+        assert torch.equal(y_k1, y_k1_h)
+        assert rel_err(y_k1.cpu().numpy(), yref) <= TOL
     # the device's h is within one bf16 step of the oracle's (float32 exp and reciprocal
     # against float64), and such differences are rare
     h_or = O.swiglu_bf16(raw)
