@@ -16,7 +16,8 @@ Also reported, on the same line:
            (calibrated on a plain copy), when recorded for the current kernel source
   cpu_baseline  the CPU oracle (dequantise, then a float64 product) on a bounded
            sample of the same workload, on the host cores
-  sweep    (--sweep) the decode workload at M = 1, 4, 8 and the other workloads
+  sweep    (--sweep) the decode workload at M = 1, 4, 8, the other workloads, and the
+           on-device quantiser (float32 weights in, canonical codes out)
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--sweep]
 Profiling helpers (used to write the summaries kept with the benchmark):
@@ -375,6 +376,33 @@ def main():
             del pl
             torch.cuda.empty_cache()
 
+    quant = {}
+    if args.sweep:
+        # on-device quantiser: dense float32 weights -> canonical codes and scales
+        for name in ("mxfp4_up", "int8_swiglu", "int4_asym_decode", "cb4_prefill"):
+            w_ = S.WORKLOADS[name]
+            fmt = w_["fmt"]
+            wd = torch.from_numpy(S.weights(w_)).cuda()
+            lv = None
+            if fmt == "cb4":
+                half = np.array([0.1284, 0.3881, 0.6568, 0.9424, 1.256, 1.618, 2.069, 2.733], dtype=np.float32)
+                lv = np.concatenate([-half[::-1], half]).astype(np.float32)
+            sym = w_.get("symmetric", True)
+            for _ in range(3):
+                Q.quantize(fmt, wd, w_["group"], symmetric=sym, levels=lv)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                Q.quantize(fmt, wd, w_["group"], symmetric=sym, levels=lv)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            nb = wd.numel() * 4 + (wd.numel() if fmt == "int8" else wd.numel() // 2)   # fp32 in + codes out
+            quant[name] = {"us": round(ms * 1e3, 1), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1)}
+            del wd
+            torch.cuda.empty_cache()
+
     cpu = None if args.no_cpu else cpu_baseline("int4_asym_decode", 16, args.cpu_seconds)
     rec = {
         "metric": "W4A16 linear: effective HBM GB/s at M=1-16; TFLOP/s + MFMA util at M=2048",
@@ -403,6 +431,8 @@ def main():
         rec["sweep"] = sweep
     if others:
         rec["others"] = others
+    if quant:
+        rec["quantize"] = quant
     print(json.dumps(rec), flush=True)
 
 

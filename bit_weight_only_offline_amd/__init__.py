@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "QL_INT4", "QL_MXFP4", "QL_INT8", "QL_CB4", "FORMATS", "QLinearError", "lib", "version",
-    "PackedWeight", "packed_bytes", "pack", "unpack", "dequant_tile", "workspace_bytes", "linear",
+    "PackedWeight", "packed_bytes", "quantize", "pack", "unpack", "dequant_tile", "workspace_bytes", "linear",
     "Schedule", "default_schedule", "tile_shapes", "workspace",
 ]
 
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.qlinear_packed_bytes.restype = ci
         L.qlinear_packed_bytes.argtypes = [ci, i64, i64, ci, ci, ctypes.POINTER(sz), ctypes.POINTER(sz),
                                            ctypes.POINTER(sz)]
+        L.qlinear_quantize.restype = ci
+        L.qlinear_quantize.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp, vp, vp]
         L.qlinear_pack.restype = ci
         L.qlinear_pack.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp, vp, vp, vp]
         L.qlinear_unpack.restype = ci
@@ -130,6 +132,48 @@ def packed_bytes(fmt, N: int, K: int, group: int, has_zeros: bool = False):
     _check(lib().qlinear_packed_bytes(_fmt(fmt), N, K, group, int(has_zeros), ctypes.byref(w), ctypes.byref(s),
                                       ctypes.byref(a)), "qlinear_packed_bytes")
     return w.value, s.value, a.value
+
+
+def quantize(fmt, w: torch.Tensor, group: int = 128, symmetric: bool = True, levels=None):
+    """Round-to-nearest quantisation of dense float32 device weights [N, K] into the
+    canonical arrays (codes, scales, aux) that pack() takes: aux is the uint8 zero-points
+    (asymmetric INT4), the 16 codebook levels as a CPU tensor (CB4) or None."""
+    f = _fmt(fmt)
+    if w.requires_grad:
+        raise QLinearError("inference-only operator: inputs must not require grad")
+    if w.device.type != "cuda":
+        raise QLinearError("the library runs on a HIP device only")
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise QLinearError("w must be a float32 [N, K] tensor")
+    w = w.contiguous()
+    N, K = w.shape
+    dev = w.device
+    G = {QL_MXFP4: 32, QL_CB4: 0}.get(f, group)
+    if f == QL_INT8:
+        codes = torch.empty((N, K), dtype=torch.int8, device=dev)
+    else:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    if f == QL_INT4:
+        scales = torch.empty((N, K // G), dtype=torch.float16, device=dev)
+    elif f == QL_INT8:
+        scales = torch.empty((N, K // G), dtype=torch.bfloat16, device=dev)
+    elif f == QL_MXFP4:
+        scales = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    else:
+        scales = torch.empty((N,), dtype=torch.bfloat16, device=dev)
+    zeros = torch.empty((N, K // G), dtype=torch.uint8, device=dev) if (f == QL_INT4 and not symmetric) else None
+    lv_ptr = None
+    lv = None
+    if f == QL_CB4:
+        if levels is None:
+            raise QLinearError("a codebook quantiser needs its 16 levels")
+        lv = torch.as_tensor(levels, dtype=torch.float32).cpu().contiguous()
+        if lv.numel() != 16:
+            raise QLinearError("a codebook has 16 levels")
+        lv_ptr = lv.data_ptr()
+    _check(lib().qlinear_quantize(f, N, K, G, _ptr(w), lv_ptr, _ptr(codes), _ptr(scales), _ptr(zeros), _stream(dev)),
+           "qlinear_quantize")
+    return codes, scales, (lv if f == QL_CB4 else zeros)
 
 
 def pack(fmt, N: int, K: int, group: int, codes: torch.Tensor, scales: torch.Tensor, aux=None) -> PackedWeight:

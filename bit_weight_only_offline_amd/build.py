@@ -25,6 +25,7 @@ SOURCES = [
     "ql_gemm_mxfp4.hip",
     "ql_gemm_cb4.hip",
     "ql_misc.hip",
+    "ql_quant.hip",
 ]
 
 ARCH = "gfx950"

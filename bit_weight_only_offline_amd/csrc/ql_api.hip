@@ -102,6 +102,23 @@ ql_status qlinear_pack(ql_format f, int64_t N, int64_t K, int group, const void 
     return from_hip(launch_pack(L, codes, scales, aux_in, packed_w, packed_s, packed_aux, (hipStream_t)stream));
 }
 
+ql_status qlinear_quantize(ql_format f, int64_t N, int64_t K, int group, const float *w, const float *levels,
+                           void *codes, void *scales, void *zeros, void *stream) {
+    const int has_zeros = (f == QL_INT4 && zeros != nullptr) ? 1 : 0;
+    ql_status st = check_format(f, N, K, group, has_zeros);
+    if (st != QL_OK) return st;
+    if (!w || !codes || !scales) return QL_E_ARG;
+    if (f == QL_CB4 ? (levels == nullptr || group != 0) : (levels != nullptr)) return QL_E_ARG;
+    if (f != QL_INT4 && zeros) return QL_E_ARG;
+    if (!aligned(w, 8) || !aligned(codes, 2) || !aligned(scales, f == QL_MXFP4 ? 1 : 2)) return QL_E_ALIGN;
+    if (f == QL_CB4)
+        for (int j = 0; j < 16; ++j)
+            if (!isfinite(levels[j])) return QL_E_UNSUPPORTED;
+    if (f != QL_CB4 && N * (K / group) >= (int64_t(1) << 33)) return QL_E_SHAPE;   // grid of groups / 4
+    return from_hip(launch_quantize(int(f), N, K, f == QL_CB4 ? 0 : group, has_zeros != 0, w, levels, codes, scales,
+                                    zeros, (hipStream_t)stream));
+}
+
 ql_status qlinear_unpack(ql_format f, int64_t N, int64_t K, int group, int has_zeros, const void *packed_w,
                          const void *packed_s, const void *packed_aux, void *codes, void *scales, void *aux_out,
                          void *stream) {

@@ -14,6 +14,9 @@ hipError_t launch_unpack(const Layout &L, const void *pw, const void *ps, const 
 hipError_t launch_dequant_tile(const Layout &L, const void *pw, const void *ps, const void *paux, int64_t n0,
                                int64_t k0, int64_t tn, int64_t tk, int mode, float *out, hipStream_t st);
 
+hipError_t launch_quantize(int fmt, int64_t N, int64_t K, int group, bool zp, const float *w,
+                           const float *levels_host, void *codes, void *scales, void *zeros, hipStream_t st);
+
 // One translation unit per format family keeps the template instantiations apart.
 hipError_t launch_gemm_int4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_int8(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);

@@ -114,6 +114,39 @@ ql_status qlinear_pack(ql_format f, int64_t N, int64_t K, int group,
                        void *packed_w, void *packed_s, void *packed_aux, void *stream);
 
 /*
+ * On-device round-to-nearest quantiser: dense weights -> the canonical arrays that
+ * qlinear_pack() takes (the step before the offline pack: quantising a dense
+ * high-precision weight, piper-kernels package description, "ConvRot INT8", from_hp;
+ * per-group amax, scale and rint to the grid as the offline packer pack_pairnib of
+ * selective_state_update_pairnib.py does).  Every operation is IEEE float32 with
+ * round-to-nearest-even, in this order:
+ *   INT4 symmetric   s = fp16(amax/7),  q = clamp(rint(w/s), -8, 7)
+ *   INT4 asymmetric  lo = min(min w, 0), hi = max(max w, 0), s = fp16((hi-lo)/15),
+ *                    z = clamp(rint(-lo/s), 0, 15), q = clamp(rint(w/s) + z, 0, 15)
+ *   INT8             s = bf16(amax/127), q = clamp(rint(w/s), -127, 127)
+ *   MXFP4            e = floor(log2 amax) - 2 in [-127, 127] (0 for a zero block);
+ *                    element = nearest E2M1 value of w * 2^-e (ties to the even code,
+ *                    saturating at 6, no negative zero); scale code e + 127
+ *   CB4              norm = bf16 of the float64 row norm (one rounding);
+ *                    u = (w * fp32(sqrt K)) / norm; index of the nearest level (float64
+ *                    distances, ties to the lower index)
+ * A scale that rounds to zero gives codes 0 (and zero-point 0).
+ *   w          float32 [N, K] row-major (device), finite
+ *   group      as for qlinear_pack (CB4: 0)
+ *   levels     CB4: HOST pointer to the 16 float32 levels, read during the call; else NULL
+ *   codes      out: canonical codes (uint8 [N, K/2] nibbles, even k low; INT8 int8 [N, K])
+ *   scales     out: fp16 [N, K/G] (INT4), uint8 E8M0 [N, K/32] (MXFP4),
+ *              bf16 [N, K/G] (INT8), bf16 row norms [N] (CB4)
+ *   zeros      out: INT4 asymmetric uint8 [N, K/G] (0..15); NULL = symmetric INT4;
+ *              must be NULL for the other formats
+ * Alignment: w 8 bytes, codes 2 bytes, scales and zeros their element size.
+ * Errors: QL_E_SHAPE / QL_E_ARG as for qlinear_pack; QL_E_UNSUPPORTED for
+ * non-finite levels.
+ */
+ql_status qlinear_quantize(ql_format f, int64_t N, int64_t K, int group, const float *w,
+                           const float *levels, void *codes, void *scales, void *zeros, void *stream);
+
+/*
  * Inverse of qlinear_pack(): device layout -> canonical arrays, bit-exact.
  *   codes, scales   canonical outputs
  *   aux_out         INT4 with zeros: zeros [N, K/G]; CB4: float32 centroids [16]

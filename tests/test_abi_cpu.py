@@ -131,6 +131,23 @@ def test_pack_validation_before_launch(L):
     assert L.qlinear_pack(INT4, 64, 256, 128, None, FAKE, None, FAKE, FAKE, None, None) == QL_E_ARG
 
 
+def test_quantize_validation_before_launch(L):
+    lv = np.linspace(-2.0, 2.0, 16).astype(np.float32)
+    bad = lv.copy()
+    bad[5] = np.nan
+    F = QL_E_SHAPE
+    assert L.qlinear_quantize(INT4, 64, 256, 100, FAKE, None, FAKE, FAKE, None, None) == F       # group
+    assert L.qlinear_quantize(MXFP4, 64, 256, 64, FAKE, None, FAKE, FAKE, None, None) == F      # MX is 32
+    assert L.qlinear_quantize(INT8, 64, 250, 256, FAKE, None, FAKE, FAKE, None, None) == F      # K % 32
+    assert L.qlinear_quantize(CB4, 64, 256, 0, FAKE, None, FAKE, FAKE, None, None) == QL_E_ARG  # no levels
+    assert L.qlinear_quantize(CB4, 64, 256, 0, FAKE, bad.ctypes.data, FAKE, FAKE, None, None) == QL_E_UNSUPPORTED
+    assert L.qlinear_quantize(INT8, 64, 256, 256, FAKE, lv.ctypes.data, FAKE, FAKE, None, None) == QL_E_ARG
+    assert L.qlinear_quantize(MXFP4, 64, 256, 32, FAKE, None, FAKE, FAKE, FAKE, None) == QL_E_ARG   # zeros
+    assert L.qlinear_quantize(INT4, 64, 256, 128, None, None, FAKE, FAKE, None, None) == QL_E_ARG
+    assert L.qlinear_quantize(INT4, 64, 256, 128, FAKE + 4, None, FAKE, FAKE, None, None) == QL_E_ALIGN
+    assert L.qlinear_quantize(INT8, 64, 256, 256, FAKE, None, FAKE + 1, FAKE, None, None) == QL_E_ALIGN
+
+
 def test_dequant_tile_validation(L):
     assert L.qlinear_dequant_tile(INT4, 64, 256, 128, 0, FAKE, FAKE, None, 60, 0, 8, 8, 0, FAKE, None) == QL_E_SHAPE
     assert L.qlinear_dequant_tile(INT4, 64, 256, 128, 0, FAKE, FAKE, None, 0, 0, 8, 8, 2, FAKE, None) == QL_E_ARG
