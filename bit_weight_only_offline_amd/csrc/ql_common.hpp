@@ -105,13 +105,13 @@ struct GemmArgs {
 //           buffer->LDS loads (ql_gemm_lds.hpp); split-K as for kind 1.
 // PF = weight chunks in flight per wavefront (kinds 0, 1) or ring depth (kind 2).
 struct TileCfg { int kind, MT, NT, SK, PF, WK, WM, WN; };
-constexpr int NUM_TILE_CFGS = 17;
+constexpr int NUM_TILE_CFGS = 19;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {0, 1, 1, 0, 4, 8, 1, 1}, {0, 1, 2, 0, 4, 8, 1, 1}, {0, 1, 4, 0, 4, 4, 1, 1}, {0, 1, 1, 0, 8, 4, 1, 1},
     {1, 2, 2, 512, 4, 4, 1, 4}, {1, 4, 2, 256, 4, 4, 1, 4}, {1, 8, 2, 128, 2, 4, 1, 4}, {1, 8, 1, 128, 4, 4, 1, 4},
     {2, 8, 3, 0, 3, 1, 1, 4}, {2, 8, 4, 0, 3, 1, 1, 4}, {2, 4, 4, 0, 3, 1, 2, 2}, {2, 4, 3, 0, 4, 1, 1, 4},
     {2, 2, 4, 0, 4, 1, 1, 4}, {2, 8, 3, 0, 3, 2, 1, 4}, {2, 8, 4, 0, 3, 2, 1, 4}, {2, 4, 4, 0, 4, 2, 1, 4},
-    {2, 4, 3, 0, 4, 2, 1, 4},
+    {2, 4, 3, 0, 4, 2, 1, 4}, {2, 2, 4, 0, 6, 1, 1, 4}, {2, 4, 3, 0, 5, 1, 1, 4},
 };
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.

@@ -85,6 +85,25 @@ __device__ inline void wait_vmcnt_rt(int n) {
 #undef QL_WAIT_CASE
 }
 
+// Activation rows of one chunk in LDS, as loaded by wave-wide direct loads of 1 KiB.
+// A row of the chunk (chunk_k(FMT) bf16) is P 16-byte pieces; one load covers RPI whole
+// rows, so every load reads full 128-byte lines.  Piece p of row r sits at 16-byte slot
+// (r % RPI) * P + (p ^ xswz(r)) of load r / RPI: for any 16 consecutive rows and a fixed
+// piece the slots differ in their low 4 bits, so an A-fragment read (16 rows, one piece
+// each) is a conflict-free ds_read_b128.
+template <int FMT>
+struct XBlock {
+    static constexpr int P = chunk_k(FMT) * 2 / 16;   // 16 (4-bit formats) or 8 (INT8)
+    static constexpr int RPI = 64 / P;                // rows per load
+    static constexpr int NI = 16 / RPI;               // loads per 16 rows
+    static constexpr int BYTES = NI * 1024;           // bytes per 16 rows
+    __host__ __device__ static constexpr int xswz(int r) { return P == 16 ? (r & 15) : ((r >> 1) & 7); }
+    // byte offset of (row r, piece p) inside the block
+    __host__ __device__ static constexpr int slot(int r, int p) {
+        return (r / RPI) * 1024 + ((r % RPI) * P + (p ^ xswz(r))) * 16;
+    }
+};
+
 // Compiler-only fence: no memory access moves across it (the hardware is not waited).
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 

@@ -8,8 +8,9 @@
 // wavefronts per SIMD hide each other's LDS and decode latency); their accumulators are
 // added in LDS, in a fixed order, before the epilogue.  One ring stage holds one chunk
 // of the input dimension (128 inputs, 64 for INT8):
-//   A  [k-step][8-wide slice][row] x 16 bytes: the A-fragment order, so each lane's
-//      fragment is one conflict-free ds_read_b128;
+//   A  the tile's activation rows, loaded as whole row pieces of the chunk (full
+//      128-byte lines per load) and XOR-swizzled so that each lane's fragment is one
+//      conflict-free ds_read_b128 (XBlock);
 //   B  the workgroup's packed 1 KiB weight tiles, copied verbatim (lane l's 16 bytes
 //      land at l*16, exactly where the lane that decodes them reads).
 // Per stage every wavefront waits for its own loads (s_waitcnt vmcnt), one barrier makes
@@ -62,7 +63,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     constexpr int NB = NTT;                         // wave-wide B loads per stage
     static_assert(NA % W == 0, "activation loads split evenly over the wavefronts");
 
-    static_assert(S >= 2 && S <= 4, "ring depth");
+    static_assert(S >= 2 && S <= 6, "ring depth");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -88,6 +89,15 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     const int kz = blockIdx.y;
     const int kc0 = kz * a.cps;
     const int nck = min(a.kchunks - kc0, a.cps);
+    // Each workgroup walks its chunks starting at its own offset (a multiple of the group
+    // span, wrapping around), spread evenly over the workgroups that share an XCD: a chunk
+    // of activations or weights is then first fetched into the XCD's L2 by one workgroup
+    // while the others that share it read it later as L2 hits, instead of every
+    // workgroup waiting on the same misses in lockstep.
+    constexpr int SPAN = (INTF && GS > STEPS) ? GS / STEPS : 1;
+    const int per_xcd = (total % 8 == 0) ? total / 8 : total;
+    const int rot = (nck > 0) ? int(((int64_t(lin % per_xcd) * nck) / per_xcd) / SPAN) * SPAN : 0;
+    auto chunk_of = [&](int i) { return kc0 + (i + rot < nck ? i + rot : i + rot - nck); };
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint32_t(int64_t(a.M) * a.ldx * 2));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
@@ -117,10 +127,11 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     int a_k[NA / W];
 #pragma unroll
     for (int q = 0; q < NA / W; ++q) {
-        const int sidx = (wv + W * q) * 64 + lane;        // 16-byte slot = (block, row)
-        const int row = sidx % MP, blk = sidx / MP;
+        // load j covers rows j*RPI .. +RPI-1; this lane's row and (swizzled) piece
+        using XB = XBlock<FMT>;
+        const int row = (wv + W * q) * XB::RPI + lane / XB::P;
         const int m = m0 + row;
-        a_k[q] = 32 * (blk >> 2) + 8 * (blk & 3);
+        a_k[q] = 8 * ((lane % XB::P) ^ XB::xswz(row));
         a_off[q] = (m < a.M) ? (uint32_t(m) * uint32_t(a.ldx) + uint32_t(a_k[q])) * 2u : 0x80000000u;
     }
     uint32_t b_off[NBW];
@@ -153,7 +164,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
 
     // issue the loads of chunk i (relative) into ring buffer buf
     auto issue = [&](int i, int buf) {
-        const int kc = kc0 + i;
+        const int kc = chunk_of(i);
         uint8_t *base = lds + buf * STAGE;
         const int kbase = kc * CH;
         const bool whole = kbase + CH <= a.K;               // wave-uniform: no input past K
@@ -189,7 +200,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     const bf16x8 ones = as_bf16x8(ones_u);
 
     auto compute = [&](int i, int buf) {
-        const int kc = kc0 + i;
+        const int kc = chunk_of(i);
         const uint8_t *A = lds + buf * STAGE;
         const uint8_t *Bt = A + A_BYTES;
         const uint8_t *sc = A + A_BYTES + B_BYTES + wv * SCW;
@@ -214,7 +225,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
             bf16x8 af[MTW];
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt)
-                af[mt] = *reinterpret_cast<const bf16x8 *>(A + ((t * 4 + g) * MP + (wm * MTW + mt) * 16 + c) * 16);
+                af[mt] = *reinterpret_cast<const bf16x8 *>(A + XBlock<FMT>::slot((wm * MTW + mt) * 16 + c, 4 * t + g));
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 u32x4 bw;
@@ -281,7 +292,9 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
             if (i < nck) {
                 // loads issued after chunk i's: those of chunks i+1 .. min(i+S-2, nck-1)
                 const int later = min(S - 2, nck - 1 - i);
-                if (later >= 2) wait_vmcnt<2 * PER_STAGE>();
+                if (later >= 4) wait_vmcnt<4 * PER_STAGE>();
+                else if (later == 3) wait_vmcnt<3 * PER_STAGE>();
+                else if (later == 2) wait_vmcnt<2 * PER_STAGE>();
                 else if (later == 1) wait_vmcnt<PER_STAGE>();
                 else wait_vmcnt<0>();
                 ring_barrier();

@@ -23,19 +23,6 @@
 
 namespace ql {
 
-// Activation block of one chunk in LDS: 16 rows x chunk_k(FMT) bf16, as NI wave-wide
-// loads of 1 KiB.  A row of the chunk is P 16-byte pieces; one load covers RPI rows.
-// Piece p of row r sits at 16-byte slot (r % RPI) * P + (p ^ xswz(r)) of load r / RPI.
-template <int FMT>
-struct XBlock {
-    static constexpr int P = chunk_k(FMT) * 2 / 16;   // 16 (4-bit formats) or 8 (INT8)
-    static constexpr int RPI = 64 / P;                // rows per load
-    static constexpr int NI = 16 / RPI;               // loads per chunk
-    static constexpr int BYTES = NI * 1024;
-    // distinct low 4 bits of the slot for the 16 rows of one fragment read
-    __device__ static constexpr int xswz(int r) { return P == 16 ? (r & 15) : ((r >> 1) & 7); }
-};
-
 template <int FMT, bool ZP, int GS, int NT, int WK, int PF>
 __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int CH = chunk_k(FMT);
@@ -89,7 +76,7 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     uint32_t xfrag[STEPS];
 #pragma unroll
     for (int t = 0; t < STEPS; ++t)
-        xfrag[t] = uint32_t(X_OFF + (c / XB::RPI) * 1024 + ((c % XB::RPI) * XB::P + ((4 * t + g) ^ XB::xswz(c))) * 16);
+        xfrag[t] = uint32_t(X_OFF + XB::slot(c, 4 * t + g));
     // scale / zero-point words: word e of a chunk's scale block is word (e % 8) of the
     // record of tile e / (8 SPC), group slot (e / 8) % SPC (MXFP4: column e % 16 of tile
     // e / 16); zero-point words likewise with 2 words per record
