@@ -83,7 +83,14 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     const int b = blockIdx.x;
     const int lin = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
     const int nblocks = (a.ntiles + NTT - 1) / NTT;
-    const int mtile = lin / nblocks, nblock = lin % nblocks;
+    // few row blocks (small M): the row blocks of one column block are consecutive, so
+    // they run on the same XCD and its L2 serves the weight tiles to all of them (the
+    // activations are small and shared by every workgroup anyway); otherwise the column
+    // blocks of one row block are consecutive and share the activation rows
+    const int mtiles = (a.M + MP - 1) / MP;
+    const bool mfast = mtiles <= 4;
+    const int mtile = mfast ? lin % mtiles : lin / nblocks;
+    const int nblock = mfast ? lin / mtiles : lin % nblocks;
     const int m0 = mtile * MP;
     const int nt0 = nblock * NTT;
     const int kz = blockIdx.y;
