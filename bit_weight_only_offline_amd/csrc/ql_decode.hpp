@@ -120,6 +120,20 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// h = bf16(up * silu(gate)) for two packed bf16 pairs, float32 math, one rounding (the
+// same function wherever the SwiGLU input stage runs, so every path forms the same h)
+__device__ inline uint32_t swiglu_pair(uint32_t up2, uint32_t gate2) {
+    float h[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float u = bf16_bits_to_f32((up2 >> (16 * e)) & 0xFFFFu);
+        const float g = bf16_bits_to_f32((gate2 >> (16 * e)) & 0xFFFFu);
+        h[e] = u * (g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)));
+    }
+    return pack_bf16x2(h[0], h[1]);
+}
+
+
 __device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -29,17 +29,6 @@
 
 namespace ql {
 
-__device__ inline uint32_t swiglu_pair(uint32_t up2, uint32_t gate2) {
-    float h[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const float u = bf16_bits_to_f32((up2 >> (16 * e)) & 0xFFFFu);
-        const float g = bf16_bits_to_f32((gate2 >> (16 * e)) & 0xFFFFu);
-        h[e] = u * (g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)));
-    }
-    return pack_bf16x2(h[0], h[1]);
-}
-
 __device__ inline float epilogue_value(const GemmArgs &a, float v, int n, float rs) {
     if (a.aux) v *= rs;
     if (a.bias) v += bf16_bits_to_f32(a.bias[n]);

@@ -183,17 +183,18 @@ def test_forward_parity(case, M):
 
 
 def _device_h(Q, raw, K):
-    """h = bf16(up * silu(gate)) as the device forms it: the SwiGLU prologue writes it to
-    the head of the workspace (a shape with many column blocks always uses it)."""
+    """h = bf16(up * silu(gate)) as the device forms it: with a ring-tile schedule the
+    SwiGLU prologue writes it to the head of the workspace."""
     M = raw.shape[0]
-    N = 1024                                   # 64 column tiles: never fused
+    N = 1024
     w = np.zeros((N, K), dtype=np.float32)
     canon = quantize("int4", w, 128, True)
     codes, scales, aux = to_device("int4", canon)
     pw = Q.pack("int4", N, K, 128, codes, scales, aux)
-    nbytes = Q.workspace_bytes("int4", M, N, K, 128, "swiglu")
+    sched = (12, 1)                            # ring tiles: never fused, h materialised
+    nbytes = Q.workspace_bytes("int4", M, N, K, 128, "swiglu", sched)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    Q.linear(bf16_tensor(raw), pw, act="swiglu", workspace=ws)
+    Q.linear(bf16_tensor(raw), pw, act="swiglu", workspace=ws, schedule=sched)
     torch.cuda.synchronize()
     return ws[: M * K * 2].view(torch.bfloat16).view(M, K).clone()
 
@@ -201,8 +202,8 @@ def _device_h(Q, raw, K):
 @pytest.mark.parametrize("fmt,G", [("int8", 256), ("int4", 128), ("mxfp4", 32), ("cb4", 0)])
 @pytest.mark.parametrize("M,N", [(1, 40), (16, 40), (70, 40), (40, 300), (130, 600)])
 def test_swiglu_fused_equals_materialised(fmt, G, M, N):
-    """The SwiGLU input stage (fused into activation staging for narrow outputs, a
-    one-pass prologue otherwise) computes the same linear as materialising
+    """The SwiGLU input stage (fused into the tile kernel's activation staging for narrow
+    outputs, a one-pass prologue otherwise) computes the same linear as materialising
     h = bf16(up * silu(gate)) first (piper-kernels, "ConvRot INT8"): bit-identical to the
     linear of the device's own h, and within the tolerance of the oracle."""
     Q = _lib()
