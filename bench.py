@@ -21,7 +21,8 @@ Also reported, on the same line:
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--sweep]
 Profiling helpers (used to write the summaries kept with the benchmark):
-  python bench.py --probe              copy calibration + 20 decode dispatches, no timing
+  python bench.py --probe [decode|prefill]   copy calibration + 20 decode dispatches, or
+                                       20 prefill dispatches; no timing
   python bench.py --summarize-trace D  per-kernel durations from a rocprofv3 CSV trace
   python bench.py --summarize-pmc F W  traffic per dispatch from FETCH_SIZE / WRITE_SIZE runs
 """
@@ -259,14 +260,28 @@ def cpu_baseline(wl_name, M, seconds=10.0):
                       f"{dt * 1e3:.1f} ms each"}
 
 
-def probe():
-    """Counter-collection workload: a plain device copy of COPY_BYTES (the calibration of
-    FETCH_SIZE / WRITE_SIZE) and 20 dispatches of the decode step; no timing."""
+def probe(which="decode"):
+    """Counter-collection workload, no timing.  decode: a plain device copy of COPY_BYTES
+    (the calibration of FETCH_SIZE / WRITE_SIZE) and 20 dispatches of the decode step;
+    prefill: 20 dispatches of the codebook prefill (M = 2048)."""
     import torch
 
     import bit_weight_only_offline_amd as Q
     import synthetic as S
     torch.cuda.set_device(0)
+    if which == "prefill":
+        wl5 = S.WORKLOADS["cb4_prefill"]
+        pool5 = _pool(Q, "cb4", wl5["N"], wl5["K"], 0, True, 5, 256 << 20)
+        x5 = torch.from_numpy(S.activations(wl5, 2048)).cuda().to(torch.bfloat16)
+        out = torch.empty((2048, wl5["N"]), dtype=torch.bfloat16, device="cuda")
+        ws = torch.zeros(max(Q.workspace_bytes("cb4", 2048, wl5["N"], wl5["K"], 0), 256), dtype=torch.uint8,
+                         device="cuda")
+        for i in range(20):
+            Q.linear(x5, pool5[i % len(pool5)], out=out, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"probe: codebook prefill M=2048 x20 ({Q.default_schedule('cb4', 2048, wl5['N'], wl5['K'], 0)})",
+              flush=True)
+        return
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -294,7 +309,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also M = 1, 4, 8 and every other workload shape")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--probe", action="store_true")
+    ap.add_argument("--probe", nargs="?", const="decode", choices=("decode", "prefill"))
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -313,7 +328,7 @@ def main():
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.probe:
-        probe()
+        probe(args.probe)
         return
 
     import torch
