@@ -16,8 +16,9 @@ Also reported, on the same line:
            (calibrated on a plain copy), when recorded for the current kernel source
   cpu_baseline  the CPU oracle (dequantise, then a float64 product) on a bounded
            sample of the same workload, on the host cores
-  sweep    (--sweep) the decode workload at M = 1, 4, 8, the other workloads, and the
-           on-device quantiser (float32 weights in, canonical codes out)
+  sweep    (--sweep) the decode workload at M = 1, 4, 8, the other workloads, the grouped
+           (mixture-of-experts) linear, and the on-device quantiser (float32 weights in,
+           canonical codes out)
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--sweep]
 Profiling helpers (used to write the summaries kept with the benchmark):
@@ -391,6 +392,58 @@ def main():
             del pl
             torch.cuda.empty_cache()
 
+    moe = {}
+    if args.sweep:
+        # mixture of experts: eight MXFP4 experts of the down projection (4096 x 14336),
+        # tokens routed uniformly at random (seeded); weights of the used experts from HBM
+        E, N_, K_ = 8, 4096, 14336
+        rng = np.random.default_rng(12)
+        c, s_, _ = _canonical("mxfp4", N_, K_, 32, True, 12)
+        pe = Q.pack_experts("mxfp4", N_, K_, 32, [(c, s_, None)] * E)
+        per_e = pe.w.numel() // E + pe.s.numel() // E
+        copies = max(1, int(np.ceil(POOL_BYTES / (per_e * E))))
+        pes = [pe] + [Q.PackedExperts(pe.fmt, E, N_, K_, 32, 0, pe.w.clone(), pe.s.clone(), None)
+                      for _ in range(copies - 1)]
+        for T in (16, 256):
+            cnt = np.bincount(rng.integers(0, E, T), minlength=E).astype(np.int32)
+            cnt_t = torch.from_numpy(cnt).cuda()
+            xm = torch.from_numpy(S.to_bf16_values(rng.standard_normal((T, K_)).astype(np.float32))).cuda().to(
+                torch.bfloat16)
+            outm = torch.empty((T, N_), dtype=torch.bfloat16, device="cuda")
+            wsm = torch.zeros(max(Q.grouped_workspace_bytes("mxfp4", T, E, N_, K_, 32), 256), dtype=torch.uint8,
+                              device="cuda")
+
+            def run_moe(i):
+                Q.grouped_linear(xm, pes[i % len(pes)], cnt_t, out=outm, workspace=wsm)
+
+            for i in range(5):
+                run_moe(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            steps = 40
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(g, stream=st):
+                    for i in range(steps):
+                        run_moe(i)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            used = int((cnt > 0).sum())
+            nb = used * per_e + T * K_ * 2 + T * N_ * 2
+            moe[f"mxfp4_down_E8/T{T}"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                                          "experts_used": used}
+            del g
+        del pes, pe
+        torch.cuda.empty_cache()
+
     quant = {}
     if args.sweep:
         # on-device quantiser: dense float32 weights -> canonical codes and scales
@@ -448,6 +501,8 @@ def main():
         rec["others"] = others
     if quant:
         rec["quantize"] = quant
+    if moe:
+        rec["moe"] = moe
     print(json.dumps(rec), flush=True)
 
 

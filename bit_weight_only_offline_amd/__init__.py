@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "QL_INT4", "QL_MXFP4", "QL_INT8", "QL_CB4", "FORMATS", "QLinearError", "lib", "version",
     "PackedWeight", "packed_bytes", "quantize", "pack", "unpack", "dequant_tile", "workspace_bytes", "linear",
-    "Schedule", "default_schedule", "tile_shapes", "workspace",
+    "Schedule", "default_schedule", "tile_shapes", "workspace", "PackedExperts", "pack_experts",
+    "grouped_workspace_bytes", "grouped_linear",
 ]
 
 QL_INT4, QL_MXFP4, QL_INT8, QL_CB4 = 0, 1, 2, 3
@@ -53,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.qlinear_packed_bytes.restype = ci
         L.qlinear_packed_bytes.argtypes = [ci, i64, i64, ci, ci, ctypes.POINTER(sz), ctypes.POINTER(sz),
                                            ctypes.POINTER(sz)]
+        L.qlinear_grouped_workspace_bytes.restype = ci
+        L.qlinear_grouped_workspace_bytes.argtypes = [ci, i64, i64, i64, i64, ci, ctypes.POINTER(sz)]
+        L.qlinear_grouped_forward.restype = ci
+        L.qlinear_grouped_forward.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, vp, ci, ci, ci, vp, vp, ci, vp, sz, vp]
         L.qlinear_quantize.restype = ci
         L.qlinear_quantize.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp, vp, vp]
         L.qlinear_pack.restype = ci
@@ -282,8 +287,8 @@ _WS = {}
 
 
 def workspace(device, nbytes: int) -> torch.Tensor:
-    """A zero-initialised workspace of at least nbytes on device, reused across calls
-    (the library leaves its arrival counters at zero after every call)."""
+    """A shared workspace of at least nbytes on device, reused across calls (the library
+    does not depend on its contents on entry)."""
     d = torch.device(device)
     key = (d.type, d.index if d.index is not None else torch.cuda.current_device())
     ws = _WS.get(key)
@@ -293,12 +298,15 @@ def workspace(device, nbytes: int) -> torch.Tensor:
     return ws
 
 
+_shared_workspace = workspace
+
+
 def linear(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, act=None,
            out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None, schedule=None) -> torch.Tensor:
     """Y = A . D(Wq)^T + b for bf16 x [..., K] (or [..., 2K] = [up | gate] with act="swiglu").
 
-    workspace: a zero-initialised uint8 device buffer that stays owned by the caller and
+    workspace: a uint8 device buffer (any contents) that stays owned by the caller and
     may be reused (a shared one per device is used when omitted).  schedule: (tile,
     splits) or a Schedule to override the automatic choice.  Inference only: inputs that
     require grad are rejected."""
@@ -328,7 +336,7 @@ def linear(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, 
     ws_need = workspace_bytes(pw.fmt, M, pw.N, pw.K, pw.group, act, schedule)
     if ws_need:
         if workspace is None:
-            workspace = globals()["workspace"](x.device, ws_need)
+            workspace = _shared_workspace(x.device, ws_need)
         elif workspace.numel() < ws_need or workspace.device != x.device:
             raise QLinearError(f"workspace needs {ws_need} bytes on {x.device}")
     _check(lib().qlinear_forward_ex(_ptr(x2), M, pw.N, pw.K, _ptr(pw.w), _ptr(pw.s), _ptr(pw.aux), pw.fmt,
@@ -337,3 +345,95 @@ def linear(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, 
                                     _ptr(workspace) if ws_need else None, ws_need if ws_need else 0,
                                     _sched(schedule), _stream(x.device)), "qlinear_forward")
     return out.reshape(*lead, pw.N)
+
+
+@dataclass
+class PackedExperts:
+    """E experts' packed weights back to back in one set of device buffers."""
+    fmt: int
+    E: int
+    N: int
+    K: int
+    group: int
+    has_zeros: int
+    w: torch.Tensor
+    s: torch.Tensor
+    aux: torch.Tensor | None
+
+    @property
+    def device(self) -> torch.device:
+        return self.w.device
+
+
+def pack_experts(fmt, N: int, K: int, group: int, experts) -> PackedExperts:
+    """Pack E experts, each given as canonical (codes, scales, aux) device tensors (aux as
+    for pack()), into consecutive slices of one set of buffers."""
+    f = _fmt(fmt)
+    experts = list(experts)
+    E = len(experts)
+    if E == 0:
+        raise QLinearError("no experts")
+    dev = experts[0][0].device
+    has_zeros = 1 if (f == QL_INT4 and experts[0][2] is not None) else 0
+    wb, sb, ab = packed_bytes(f, N, K, group, bool(has_zeros))
+    w = torch.empty(E * wb, dtype=torch.uint8, device=dev)
+    s = torch.empty(E * sb, dtype=torch.uint8, device=dev)
+    a = torch.empty(E * ab, dtype=torch.uint8, device=dev) if ab else None
+    keep = []
+    for e, (codes, scales, aux) in enumerate(experts):
+        codes = codes.contiguous()
+        scales = scales.contiguous()
+        aux_ptr = None
+        if f == QL_CB4:
+            lv = torch.as_tensor(aux, dtype=torch.float32).cpu().contiguous()
+            keep.append(lv)
+            aux_ptr = lv.data_ptr()
+        elif aux is not None:
+            aux = aux.contiguous()
+            keep.append(aux)
+            aux_ptr = aux.data_ptr()
+        _check(lib().qlinear_pack(f, N, K, group, _ptr(codes), _ptr(scales), aux_ptr, w.data_ptr() + e * wb,
+                                  s.data_ptr() + e * sb, None if a is None else a.data_ptr() + e * ab, _stream(dev)),
+               "qlinear_pack")
+    return PackedExperts(f, E, N, K, group, has_zeros, w, s, a)
+
+
+def grouped_workspace_bytes(fmt, T: int, E: int, N: int, K: int, group: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().qlinear_grouped_workspace_bytes(_fmt(fmt), T, E, N, K, group, ctypes.byref(n)),
+           "qlinear_grouped_workspace_bytes")
+    return n.value
+
+
+def grouped_linear(x: torch.Tensor, pe: PackedExperts, tokens_per_expert: torch.Tensor, bias=None,
+                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Mixture-of-experts linear: rows of x [T, K] grouped by expert in expert order,
+    tokens_per_expert an int32 device tensor [E]; bias bf16 [E, N] or None.  Rows past
+    the sum of the counts are left as they are in `out` (uninitialised when allocated)."""
+    if x.requires_grad or (bias is not None and bias.requires_grad):
+        raise QLinearError("inference-only operator: inputs must not require grad")
+    if x.device.type != "cuda" or pe.w.device.type != "cuda" or tokens_per_expert.device.type != "cuda":
+        raise QLinearError("the library runs on a HIP device only")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != pe.K:
+        raise QLinearError("x must be bfloat16 [T, K]")
+    if tokens_per_expert.dtype != torch.int32 or tokens_per_expert.numel() != pe.E:
+        raise QLinearError("tokens_per_expert must be int32 [E]")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != pe.E * pe.N):
+        raise QLinearError("bias must be bfloat16 [E, N]")
+    x = x.contiguous()
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, pe.N), dtype=out_dtype, device=x.device)
+    nbytes = grouped_workspace_bytes(pe.fmt, T, pe.E, pe.N, pe.K, pe.group)
+    if workspace is None:
+        workspace = _shared_workspace(x.device, nbytes)
+    elif workspace.numel() < nbytes or workspace.device != x.device:
+        raise QLinearError(f"workspace needs {nbytes} bytes on {x.device}")
+    od = 1 if out_dtype == torch.float32 else 0
+    _check(lib().qlinear_grouped_forward(_ptr(x), T, _ptr(tokens_per_expert.contiguous()), pe.E, pe.N, pe.K,
+                                         _ptr(pe.w), _ptr(pe.s), _ptr(pe.aux), pe.fmt, pe.group, pe.has_zeros,
+                                         _ptr(bias), _ptr(out), od, _ptr(workspace), workspace.numel(),
+                                         _stream(x.device)), "qlinear_grouped_forward")
+    return out
+

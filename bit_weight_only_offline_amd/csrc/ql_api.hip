@@ -184,6 +184,34 @@ ql_status plan_for(ql_format f, int64_t M, int64_t N, int64_t K, int group, int 
     return QL_OK;
 }
 
+// Grouped (mixture-of-experts) launch: the decode kernel (slots of 16 rows) or ring tiles,
+// chosen by the mean number of tokens per expert, one row-block slot per possible tile
+// (sum over experts of ceil(T_e / rows) is at most ceil(T / rows) + E), no split of the
+// input dimension across workgroups.  Workspace: the expert
+// offsets [E + 1] and the slot map [slots][2], both int32.
+struct GroupedPlan {
+    Plan plan;
+    int rows = 0;
+    size_t ws_bytes = 0;
+};
+GroupedPlan grouped_plan(int64_t T, int64_t E, int64_t N, int64_t K, ql_format f, int group) {
+    GroupedPlan g;
+    const Layout L = layout_of(f, N, K, group, 0);
+    const int64_t per = (T + E - 1) / E;
+    int cfg;
+    if (per <= 16) cfg = default_cfg(L, 16);            // decode kernel, slots of 16 rows
+    else if (per <= 48) cfg = 12;                        // 32 x 256
+    else if (per <= 96) cfg = 16;                        // 64 x 192, two waves per tile
+    else cfg = (f == QL_INT4 || f == QL_INT8) ? 8 : 13;  // 128 x 192
+    g.plan = make_plan(L, 16, cfg, 1, PLAN_CUS, false);  // column blocks, chunks per wave
+    g.rows = is_decode(cfg) ? 16 : cfg_rows(TILE_CFGS[cfg]);
+    g.plan.mtiles = int(ceil_div(T, g.rows) + E);
+    g.plan.ks = 1;
+    if (!is_decode(cfg)) g.plan.cps = int(L.kchunks);
+    g.ws_bytes = round256(size_t(E + 1) * 4) + round256(size_t(g.plan.mtiles) * 8);
+    return g;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,7 +284,7 @@ ql_status qlinear_forward_ex(const void *x, int64_t M, int64_t N, int64_t K, con
         if (!aligned(workspace, 256)) return QL_E_ALIGN;
     }
     const bool decode = is_decode(p.cfg);
-    GemmArgs a;
+    GemmArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.w = static_cast<const uint8_t *>(packed_w);
     a.s = static_cast<const uint8_t *>(packed_s);
@@ -307,6 +335,84 @@ ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K, const 
                           void *out, ql_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
     return qlinear_forward_ex(x, M, N, K, packed_w, packed_s, packed_aux, f, group, has_zeros, bias, act, out,
                               out_dtype, workspace, workspace_bytes, nullptr, stream);
+}
+
+ql_status qlinear_grouped_workspace_bytes(ql_format f, int64_t T, int64_t E, int64_t N, int64_t K, int group,
+                                          size_t *bytes) {
+    if (!bytes) return QL_E_ARG;
+    ql_status st = check_format(f, N, K, group, 0);
+    if (st != QL_OK) return st;
+    if (T < 0 || E < 0 || T >= (int64_t(1) << 31) || E >= (int64_t(1) << 20)) return QL_E_SHAPE;
+    if (T == 0 || E == 0) {
+        *bytes = 0;
+        return QL_OK;
+    }
+    *bytes = grouped_plan(T, E, N, K, f, group).ws_bytes;
+    return QL_OK;
+}
+
+ql_status qlinear_grouped_forward(const void *x, int64_t T, const int32_t *tokens_per_expert, int64_t E, int64_t N,
+                                  int64_t K, const void *packed_w, const void *packed_s, const void *packed_aux,
+                                  ql_format f, int group, int has_zeros, const void *bias, void *out,
+                                  ql_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    ql_status st = check_format(f, N, K, group, has_zeros);
+    if (st != QL_OK) return st;
+    if (out_dtype != QL_BF16 && out_dtype != QL_F32) return QL_E_ARG;
+    if (T < 0 || E < 0 || T >= (int64_t(1) << 31) || E >= (int64_t(1) << 20)) return QL_E_SHAPE;
+    if (T * K >= (int64_t(1) << 30) || T * N >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    if (T == 0 || E == 0) return QL_OK;
+    if (!x || !tokens_per_expert || !packed_w || !packed_s || !out) return QL_E_ARG;
+    if (((f == QL_CB4) || (f == QL_INT4 && has_zeros)) && !packed_aux) return QL_E_ARG;
+    if (!aligned(x, 16) || !aligned(packed_w, 16) || !aligned(packed_s, 16)) return QL_E_ALIGN;
+    if (packed_aux && !aligned(packed_aux, 16)) return QL_E_ALIGN;
+    if (!aligned(tokens_per_expert, 4) || (bias && !aligned(bias, 2))) return QL_E_ALIGN;
+    if (!aligned(out, out_dtype == QL_F32 ? 4 : 2)) return QL_E_ALIGN;
+    const Layout L = layout_of(f, N, K, group, has_zeros);
+    const GroupedPlan gp = grouped_plan(T, E, N, K, f, group);
+    if (!workspace || workspace_bytes < gp.ws_bytes) return QL_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return QL_E_ALIGN;
+    int *offsets = static_cast<int *>(workspace);
+    int *tile_map = offsets + round256(size_t(E + 1) * 4) / 4;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_moe_plan(tokens_per_expert, int(E), int(T), gp.rows, gp.plan.mtiles, offsets, tile_map, s);
+    if (e != hipSuccess) return QL_E_HIP;
+    GemmArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = static_cast<const uint8_t *>(packed_w);
+    a.s = static_cast<const uint8_t *>(packed_s);
+    a.z = (f == QL_INT4 && has_zeros) ? static_cast<const uint8_t *>(packed_aux) : nullptr;
+    a.aux = (f == QL_CB4) ? static_cast<const uint8_t *>(packed_aux) : nullptr;
+    a.bias = static_cast<const uint16_t *>(bias);
+    a.out = out;
+    a.ws = nullptr;
+    a.M = int(T);
+    a.N = int(N);
+    a.K = int(K);
+    a.ldx = int(K);
+    a.Np = int(L.Np);
+    a.ntiles = int(L.ntiles);
+    a.kchunks = int(L.kchunks);
+    a.ngroups = int(L.ngroups);
+    a.cps = gp.plan.cps;
+    a.ks = 1;
+    a.swiglu = 0;
+    a.out_f32 = out_dtype == QL_F32 ? 1 : 0;
+    a.w_bytes = uint32_t(L.w_bytes);
+    a.s_bytes = uint32_t(L.s_bytes);
+    a.z_bytes = uint32_t(L.aux_bytes);
+    a.tile_map = tile_map;
+    a.offsets = offsets;
+    a.w_stride = L.w_bytes;
+    a.s_stride = L.s_bytes;
+    a.z_stride = L.aux_bytes;
+    a.slots = gp.plan.mtiles;
+    switch (f) {
+        case QL_INT4: e = launch_gemm_int4(L, gp.plan, a, s); break;
+        case QL_INT8: e = launch_gemm_int8(L, gp.plan, a, s); break;
+        case QL_MXFP4: e = launch_gemm_mxfp4(L, gp.plan, a, s); break;
+        default: e = launch_gemm_cb4(L, gp.plan, a, s); break;
+    }
+    return from_hip(e);
 }
 
 }  // extern "C"

@@ -90,6 +90,14 @@ struct GemmArgs {
     int cps, ks;           // chunks per split, number of splits
     int swiglu, out_f32;
     uint32_t w_bytes, s_bytes, z_bytes;
+    // grouped (mixture-of-experts) mode, ring tiles only: the grid has `slots` row-block
+    // slots; tile_map[2 s] = expert of slot s (-1: unused), tile_map[2 s + 1] = its first
+    // row within the expert; expert e owns rows offsets[e] .. offsets[e+1]-1 of x and
+    // out, and its packed buffers start e * stride bytes after w, s, z (aux: e * 128)
+    const int *tile_map;   // null: dense
+    const int *offsets;
+    uint64_t w_stride, s_stride, z_stride;
+    int slots;
 };
 
 // Schedules compiled into the library.

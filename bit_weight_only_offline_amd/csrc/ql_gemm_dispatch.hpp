@@ -25,7 +25,7 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
         static bool attr_set = false;
         hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(p.nblocks), dim3(64 * t.WK), lds, st, a);
+        hipLaunchKernelGGL(kern, dim3(p.nblocks, a.tile_map ? a.slots : 1), dim3(64 * t.WK), lds, st, a);
     } else if constexpr (t.kind == 2) {
         constexpr int depth = ring_depth(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, t.PF);
         auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth>;

@@ -87,23 +87,38 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     // they run on the same XCD and its L2 serves the weight tiles to all of them (the
     // activations are small and shared by every workgroup anyway); otherwise the column
     // blocks of one row block are consecutive and share the activation rows
-    const int mtiles = (a.M + MP - 1) / MP;
+    const int mtiles = a.tile_map ? a.slots : (a.M + MP - 1) / MP;
     const bool mfast = mtiles <= 4;
     const int mtile = mfast ? lin % mtiles : lin / nblocks;
     const int nblock = mfast ? lin / mtiles : lin % nblocks;
-    const int m0 = mtile * MP;
+    int m0 = mtile * MP;
+    if (a.tile_map) {
+        // grouped: this slot's expert and row block; the expert's rows, output rows and
+        // packed buffers become the whole problem of this workgroup
+        const int e = a.tile_map[2 * mtile];
+        if (e < 0) return;                               // unused slot: the whole workgroup
+        m0 = a.tile_map[2 * mtile + 1];
+        const int r0 = a.offsets[e];
+        a.M = a.offsets[e + 1] - r0;
+        a.x += int64_t(r0) * a.ldx;
+        a.out = static_cast<uint8_t *>(a.out) + int64_t(r0) * a.N * (a.out_f32 ? 4 : 2);
+        a.w += uint64_t(e) * a.w_stride;
+        a.s += uint64_t(e) * a.s_stride;
+        if (a.z) a.z += uint64_t(e) * a.z_stride;
+        if (a.aux) a.aux += uint64_t(e) * CB_AUX_BYTES;
+        if (a.bias) a.bias += int64_t(e) * a.N;
+    }
     const int nt0 = nblock * NTT;
     const int kz = blockIdx.y;
     const int kc0 = kz * a.cps;
     const int nck = min(a.kchunks - kc0, a.cps);
-    // Each workgroup walks its chunks starting at its own offset (a multiple of the group
-    // span, wrapping around), spread evenly over the workgroups that share an XCD: a chunk
-    // of activations or weights is then first fetched into the XCD's L2 by one workgroup
-    // while the others that share it read it later as L2 hits, instead of every
-    // workgroup waiting on the same misses in lockstep.
+    // Each workgroup walks its chunks starting at an offset set by its column block (a
+    // multiple of the group span, wrapping around), so the workgroups that share a row
+    // block of activations do not all miss on the same chunk at once.  The offset depends
+    // on the column block only: a tile's summation order, hence its result, does not
+    // depend on the grid it was launched in.
     constexpr int SPAN = (INTF && GS > STEPS) ? GS / STEPS : 1;
-    const int per_xcd = (total % 8 == 0) ? total / 8 : total;
-    const int rot = (nck > 0) ? int(((int64_t(lin % per_xcd) * nck) / per_xcd) / SPAN) * SPAN : 0;
+    const int rot = (nck > 0) ? int(((int64_t(nblock % 16) * nck) / 16) / SPAN) * SPAN : 0;
     auto chunk_of = [&](int i) { return kc0 + (i + rot < nck ? i + rot : i + rot - nck); };
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint32_t(int64_t(a.M) * a.ldx * 2));

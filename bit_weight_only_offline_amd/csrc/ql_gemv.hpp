@@ -44,6 +44,22 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keep it scalar
     const int g = lane >> 4, c = lane & 15;
     const int ntb = blockIdx.x * NT;
+    if (a.tile_map) {
+        // grouped: blockIdx.y is a slot of up to 16 rows of one expert; those rows, their
+        // output rows and the expert's packed buffers become this workgroup's problem
+        const int slot = blockIdx.y;
+        const int e = a.tile_map[2 * slot];
+        if (e < 0) return;                               // unused slot: the whole workgroup
+        const int row0 = a.offsets[e] + a.tile_map[2 * slot + 1];
+        a.M = min(16, a.offsets[e + 1] - row0);
+        a.x += int64_t(row0) * a.ldx;
+        a.out = static_cast<uint8_t *>(a.out) + int64_t(row0) * a.N * (a.out_f32 ? 4 : 2);
+        a.w += uint64_t(e) * a.w_stride;
+        a.s += uint64_t(e) * a.s_stride;
+        if (a.z) a.z += uint64_t(e) * a.z_stride;
+        if (a.aux) a.aux += uint64_t(e) * CB_AUX_BYTES;
+        if (a.bias) a.bias += int64_t(e) * a.N;
+    }
     // this wavefront's run of chunks: cps per wavefront (a multiple of the group span)
     const int kc0 = wv * a.cps;
     const int nck = max(0, min(a.kchunks - kc0, a.cps));

@@ -24,5 +24,7 @@ hipError_t launch_gemm_mxfp4(const Layout &L, const Plan &p, const GemmArgs &a, 
 hipError_t launch_gemm_cb4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
 hipError_t launch_reduce(const GemmArgs &a, hipStream_t st);
 hipError_t launch_swiglu(const uint16_t *x, uint16_t *h, int M, int K, hipStream_t st);
+hipError_t launch_moe_plan(const int32_t *counts, int E, int T, int rows, int slots, int *offsets, int *tile_map,
+                           hipStream_t st);
 
 }  // namespace ql

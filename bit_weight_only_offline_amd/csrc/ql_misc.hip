@@ -57,4 +57,34 @@ hipError_t launch_swiglu(const uint16_t *x, uint16_t *h, int M, int K, hipStream
     return hipGetLastError();
 }
 
+// Grouped launch plan: expert offsets (exclusive prefix sum of the token counts, each
+// count clamped to [0, tokens left] so rows never run past T) and the slot map, expert
+// by expert in order, unused slots marked -1.  One thread: E and the slot count are small
+// and the order is then fixed.
+__global__ void moe_plan_kernel(const int32_t *__restrict__ counts, int E, int T, int rows, int slots,
+                                int *__restrict__ offsets, int *__restrict__ tile_map) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int run = 0, t = 0;
+    for (int e = 0; e < E; ++e) {
+        const int c = min(max(counts[e], 0), T - run);
+        offsets[e] = run;
+        for (int r = 0; r < c && t < slots; r += rows, ++t) {
+            tile_map[2 * t] = e;
+            tile_map[2 * t + 1] = r;
+        }
+        run += c;
+    }
+    offsets[E] = run;
+    for (; t < slots; ++t) {
+        tile_map[2 * t] = -1;
+        tile_map[2 * t + 1] = 0;
+    }
+}
+
+hipError_t launch_moe_plan(const int32_t *counts, int E, int T, int rows, int slots, int *offsets, int *tile_map,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(64), 0, st, counts, E, T, rows, slots, offsets, tile_map);
+    return hipGetLastError();
+}
+
 }  // namespace ql

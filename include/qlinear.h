@@ -244,6 +244,38 @@ ql_status qlinear_forward_ex(const void *x, int64_t M, int64_t N, int64_t K,
                              void *workspace, size_t workspace_bytes, const ql_schedule *sched,
                              void *stream);
 
+/*
+ * Grouped (mixture-of-experts) linear: every token is multiplied by its own expert's
+ * packed weight (AutoRound Kernel package description, "2. MoE (Mixture-of-Experts Grouped
+ * GEMM)": activations [total_tokens, K], per-expert weights, num_tokens_per_expert [E]
+ * int32, output [total_tokens, N]; Petit package description, "Features": fused MoE
+ * kernels for MXFP4 weights).  Tokens are grouped by expert in expert order: expert e
+ * owns rows offsets[e] .. offsets[e+1]-1 of x and out, offsets being the running sum of
+ * tokens_per_expert.
+ *   x                  bf16 [T, K] (device, 16-byte aligned)
+ *   tokens_per_expert  int32 [E] (device); read by the device, so it may be computed on
+ *                      the device in the same stream.  A negative count counts as 0 and
+ *                      counts past T are clipped, so no row beyond T is read or written;
+ *                      rows past the sum of the counts are left untouched.
+ *   packed_w/s/aux     E experts' packed buffers back to back: expert e's buffers start
+ *                      e * w_bytes (s_bytes, aux_bytes) in, with the sizes that
+ *                      qlinear_packed_bytes() gives for one expert [N, K]
+ *   bias               NULL or bf16 [E, N] (one row per expert)
+ *   out                [T, N] bf16 or float32
+ *   workspace          qlinear_grouped_workspace_bytes() bytes, 256-byte aligned (the
+ *                      expert offsets and the tile map are written there)
+ * The kernels are the LDS-ring tiles of qlinear_forward(); each workgroup takes one row
+ * block of one expert.  T = 0 or E = 0 is a no-op.
+ */
+ql_status qlinear_grouped_workspace_bytes(ql_format f, int64_t T, int64_t E, int64_t N, int64_t K,
+                                          int group, size_t *bytes);
+ql_status qlinear_grouped_forward(const void *x, int64_t T, const int32_t *tokens_per_expert,
+                                  int64_t E, int64_t N, int64_t K,
+                                  const void *packed_w, const void *packed_s, const void *packed_aux,
+                                  ql_format f, int group, int has_zeros, const void *bias,
+                                  void *out, ql_dtype out_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

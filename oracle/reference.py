@@ -393,6 +393,26 @@ def forward(fmt: str, x, canon: dict, K: int, bias=None, swiglu: bool = False) -
     return linear_ref(a, dequant(fmt, canon, K), bias)
 
 
+def forward_grouped(fmt: str, x, canons, counts, K: int, N: int, biases=None) -> np.ndarray:
+    """Mixture-of-experts linear (AutoRound Kernel package description, "2. MoE
+    (Mixture-of-Experts Grouped GEMM)": activations [total_tokens, K], per-expert weights,
+    num_tokens_per_expert [E], output [total_tokens, N]).  Tokens are grouped by expert
+    in expert order; token t of expert e's slice is multiplied by expert e's D(Wq) and
+    bias.  Counts are clipped as the library documents (negative -> 0, nothing past T);
+    rows past the sum of the counts are NaN here (the library leaves them untouched)."""
+    x = np.asarray(x, dtype=np.float32)
+    T = x.shape[0]
+    y = np.full((T, N), np.nan, dtype=np.float64)
+    run = 0
+    for e, c in enumerate(counts):
+        c = min(max(int(c), 0), T - run)
+        if c:
+            b = None if biases is None else biases[e]
+            y[run:run + c] = forward(fmt, x[run:run + c], canons[e], K, b)
+        run += c
+    return y
+
+
 def output_rows(fmt: str, x, canon: dict, K: int, rows, cols, bias=None, swiglu=False) -> np.ndarray:
     """Y[rows[i], cols[i]] one by one (float64), dequantising only the needed weight
     rows: for sampled checks of large shapes."""

@@ -148,6 +148,28 @@ def test_quantize_validation_before_launch(L):
     assert L.qlinear_quantize(INT8, 64, 256, 256, FAKE, None, FAKE + 1, FAKE, None, None) == QL_E_ALIGN
 
 
+def test_grouped_validation_before_launch(L):
+    need = ctypes.c_size_t()
+    assert L.qlinear_grouped_workspace_bytes(MXFP4, 256, 8, 4096, 14336, 32, ctypes.byref(need)) == QL_OK
+    assert need.value > 0 and need.value % 256 == 0
+    assert L.qlinear_grouped_workspace_bytes(MXFP4, 0, 8, 4096, 14336, 32, ctypes.byref(need)) == QL_OK
+    assert need.value == 0
+
+    def g(T=256, cnt=FAKE, E=8, N=4096, K=4096, w=FAKE, s=FAKE, aux=None, f=INT4, G=128, z=0, bias=None,
+          out=FAKE, od=0, ws=FAKE, wsb=1 << 30):
+        return L.qlinear_grouped_forward(FAKE, T, cnt, E, N, K, w, s, aux, f, G, z, bias, out, od, ws, wsb, None)
+
+    assert g(T=0) == QL_OK and g(E=0) == QL_OK            # no-ops
+    assert g(cnt=None) == QL_E_ARG
+    assert g(cnt=FAKE + 2) == QL_E_ALIGN
+    assert g(G=100) == QL_E_SHAPE
+    assert g(T=-1) == QL_E_SHAPE
+    assert g(od=2) == QL_E_ARG
+    assert g(f=CB4, G=0) == QL_E_ARG                      # codebook record required
+    assert g(ws=None, wsb=0) == QL_E_WORKSPACE
+    assert g(ws=FAKE + 16) == QL_E_ALIGN
+
+
 def test_dequant_tile_validation(L):
     assert L.qlinear_dequant_tile(INT4, 64, 256, 128, 0, FAKE, FAKE, None, 60, 0, 8, 8, 0, FAKE, None) == QL_E_SHAPE
     assert L.qlinear_dequant_tile(INT4, 64, 256, 128, 0, FAKE, FAKE, None, 0, 0, 8, 8, 2, FAKE, None) == QL_E_ARG

@@ -354,6 +354,30 @@ def test_linear_brute_force_exact_rationals(fmt):
     assert y.shape == (M, N)
 
 
+def test_grouped_brute_force_exact_rationals():
+    """The grouped (MoE) product row by row in exact rational arithmetic: each token's
+    row uses its own expert's weights, experts in order, clipped counts."""
+    rng = np.random.default_rng(21)
+    T, N, K, E = 7, 3, 128, 4
+    x = S.to_bf16_values(rng.standard_normal((T, K)).astype(np.float32))
+    canons, dws, biases = [], [], []
+    for e in range(E):
+        w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        canons.append(O.quantize("mxfp4", w))
+        dws.append(O.dequant("mxfp4", canons[-1], K))
+        biases.append(S.to_bf16_values((rng.standard_normal(N) * 0.01).astype(np.float32)))
+    counts = [2, 0, -3, 9]           # expert 2 counts as empty, expert 3 is clipped to 5 rows
+    y = O.forward_grouped("mxfp4", x, canons, counts, K, N, biases)
+    owner = [0, 0, 3, 3, 3, 3, 3]
+    for t in range(T):
+        ex = _frac_linear(x[t:t + 1], dws[owner[t]], biases[owner[t]])[0]
+        for n in range(N):
+            assert abs(Fraction(y[t, n]) - ex[n]) <= abs(ex[n]) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+    # fewer tokens than rows: the rest stays unset
+    y2 = O.forward_grouped("mxfp4", x, canons, [1, 1, 0, 0], K, N)
+    assert np.all(np.isnan(y2[2:])) and np.all(np.isfinite(y2[:2]))
+
+
 def test_output_rows_matches_full_forward():
     rng = np.random.default_rng(12)
     wl = S.small("int8_swiglu", N=64, K=512)
