@@ -264,8 +264,9 @@ ql_status qlinear_forward_ex(const void *x, int64_t M, int64_t N, int64_t K,
  *   out                [T, N] bf16 or float32
  *   workspace          qlinear_grouped_workspace_bytes() bytes, 256-byte aligned (the
  *                      expert offsets and the tile map are written there)
- * The kernels are the LDS-ring tiles of qlinear_forward(); each workgroup takes one row
- * block of one expert.  T = 0 or E = 0 is a no-op.
+ * The kernels are those of qlinear_forward(): the decode kernel in slots of 16 rows when
+ * the experts average at most 16 tokens, else the LDS-ring tiles; each workgroup takes one
+ * row block of one expert.  T = 0 or E = 0 is a no-op.
  */
 ql_status qlinear_grouped_workspace_bytes(ql_format f, int64_t T, int64_t E, int64_t N, int64_t K,
                                           int group, size_t *bytes);
