@@ -17,8 +17,8 @@ Also reported, on the same line:
   cpu_baseline  the CPU oracle (dequantise, then a float64 product) on a bounded
            sample of the same workload, on the host cores
   sweep    (--sweep) the decode workload at M = 1, 4, 8, the other workloads, the grouped
-           (mixture-of-experts) linear, and the on-device quantiser (float32 weights in,
-           canonical codes out)
+           (mixture-of-experts) linear, the on-device quantiser (float32 weights in,
+           canonical codes out) and the in-place INT8 low-rank merge
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--sweep]
 Profiling helpers (used to write the summaries kept with the benchmark):
@@ -471,6 +471,36 @@ def main():
             del wd
             torch.cuda.empty_cache()
 
+    merge = {}
+    if args.sweep:
+        # in-place INT8 low-rank merge on the INT8 SwiGLU layer's weight (8192 x 28672,
+        # group 256), rank 16 and 64, nearest and stochastic rounding
+        w_ = S.WORKLOADS["int8_swiglu"]
+        N_, K_, G_ = w_["N"], w_["K"], w_["group"]
+        rng = np.random.default_rng(31)
+        pw = Q.pack("int8", N_, K_, G_, *_canonical("int8", N_, K_, G_, True, 31))
+        for r in (16, 64):
+            a = torch.from_numpy(S.to_bf16_values((rng.standard_normal((N_, r)) * 1e-3).astype(np.float32))).cuda()
+            b = torch.from_numpy(S.to_bf16_values((rng.standard_normal((r, K_)) * 1e-3).astype(np.float32))).cuda()
+            a, b = a.to(torch.bfloat16), b.to(torch.bfloat16)
+            for seed in (None, 1):
+                for _ in range(2):
+                    Q.int8_addmm_(pw, a, b, alpha=1.0, rounding_seed=seed)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(5):
+                    Q.int8_addmm_(pw, a, b, alpha=1.0, rounding_seed=seed)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 5
+                nb = 2 * N_ * K_ + 4 * N_ * (K_ // G_) + 2 * r * (N_ + K_)    # codes and scales read and written
+                merge[f"r{r}/{'nearest' if seed is None else 'stochastic'}"] = {
+                    "us": round(ms * 1e3, 1), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                    "GFLOP/s": round(2.0 * N_ * K_ * r / (ms * 1e-3) / 1e9, 1)}
+        del pw
+        torch.cuda.empty_cache()
+
     cpu = None if args.no_cpu else cpu_baseline("int4_asym_decode", 16, args.cpu_seconds)
     rec = {
         "metric": "W4A16 linear: effective HBM GB/s at M=1-16; TFLOP/s + MFMA util at M=2048",
@@ -501,6 +531,8 @@ def main():
         rec["others"] = others
     if quant:
         rec["quantize"] = quant
+    if merge:
+        rec["int8_merge"] = merge
     if moe:
         rec["moe"] = moe
     print(json.dumps(rec), flush=True)

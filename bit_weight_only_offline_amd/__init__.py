@@ -18,7 +18,7 @@ __all__ = [
     "QL_INT4", "QL_MXFP4", "QL_INT8", "QL_CB4", "FORMATS", "QLinearError", "lib", "version",
     "PackedWeight", "packed_bytes", "quantize", "pack", "unpack", "dequant_tile", "workspace_bytes", "linear",
     "Schedule", "default_schedule", "tile_shapes", "workspace", "PackedExperts", "pack_experts",
-    "grouped_workspace_bytes", "grouped_linear",
+    "grouped_workspace_bytes", "grouped_linear", "int8_addmm_",
 ]
 
 QL_INT4, QL_MXFP4, QL_INT8, QL_CB4 = 0, 1, 2, 3
@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.qlinear_grouped_forward.restype = ci
         L.qlinear_grouped_forward.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, vp, ci, ci, ci, vp, vp, ci, vp, sz, vp]
         L.qlinear_quantize.restype = ci
+        L.qlinear_int8_addmm.restype = ci
+        L.qlinear_int8_addmm.argtypes = [i64, i64, ci, vp, vp, vp, vp, i64, ctypes.c_float, ctypes.c_float, ci,
+                                         ctypes.c_uint64, vp]
         L.qlinear_quantize.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp, vp, vp]
         L.qlinear_pack.restype = ci
         L.qlinear_pack.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp, vp, vp, vp]
@@ -210,6 +213,35 @@ def pack(fmt, N: int, K: int, group: int, codes: torch.Tensor, scales: torch.Ten
     _check(lib().qlinear_pack(f, N, K, group, _ptr(codes), _ptr(scales), aux_ptr, _ptr(w), _ptr(s), _ptr(a),
                               _stream(dev)), "qlinear_pack")
     return PackedWeight(f, N, K, group, has_zeros, w, s, a)
+
+
+def int8_addmm_(pw: PackedWeight, mat1: torch.Tensor, mat2: torch.Tensor, alpha: float = 1.0, beta: float = 1.0,
+                rounding_seed: int | None = None) -> PackedWeight:
+    """In place: pw <- beta * pw + alpha * (mat1 @ mat2), requantised to INT8 in the same
+    device buffers.  mat1 bf16 [N, r] (the adapter's B), mat2 bf16 [r, K] (its A).
+    rounding_seed: None for nearest rounding, else an unsigned 64-bit seed for the
+    stochastic choice between the two neighbouring codes.  Returns pw."""
+    if pw.fmt != QL_INT8:
+        raise QLinearError("the low-rank merge updates INT8 weights")
+    for t in (mat1, mat2):
+        if t.requires_grad:
+            raise QLinearError("inference-only operator: inputs must not require grad")
+        if t.device != pw.device:
+            raise QLinearError("mat1 and mat2 must be on the weight's device")
+        if t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise QLinearError("mat1 and mat2 must be bf16 matrices")
+    r = mat1.shape[1]
+    if tuple(mat1.shape) != (pw.N, r) or tuple(mat2.shape) != (r, pw.K):
+        raise QLinearError(f"mat1 must be [N, r] and mat2 [r, K]; got {tuple(mat1.shape)} and {tuple(mat2.shape)}")
+    if rounding_seed is not None and not 0 <= int(rounding_seed) < 2 ** 64:
+        raise QLinearError("rounding_seed must be an unsigned 64-bit integer")
+    m1, m2 = mat1.contiguous(), mat2.contiguous()
+    _check(lib().qlinear_int8_addmm(pw.N, pw.K, pw.group, _ptr(pw.w), _ptr(pw.s), _ptr(m1) if r else None,
+                                    _ptr(m2) if r else None, r,
+                                    float(alpha), float(beta), 0 if rounding_seed is None else 1,
+                                    0 if rounding_seed is None else int(rounding_seed), _stream(pw.device)),
+           "qlinear_int8_addmm")
+    return pw
 
 
 def unpack(pw: PackedWeight):

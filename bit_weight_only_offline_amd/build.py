@@ -26,6 +26,7 @@ SOURCES = [
     "ql_gemm_cb4.hip",
     "ql_misc.hip",
     "ql_quant.hip",
+    "ql_lora.hip",
 ]
 
 ARCH = "gfx950"

@@ -119,6 +119,23 @@ ql_status qlinear_quantize(ql_format f, int64_t N, int64_t K, int group, const f
                                     zeros, (hipStream_t)stream));
 }
 
+ql_status qlinear_int8_addmm(int64_t N, int64_t K, int group, void *packed_w, void *packed_s, const void *mat1,
+                             const void *mat2, int64_t rank, float alpha, float beta, int stochastic, uint64_t seed,
+                             void *stream) {
+    ql_status st = check_format(QL_INT8, N, K, group, 0);
+    if (st != QL_OK) return st;
+    if (!packed_w || !packed_s) return QL_E_ARG;
+    if (rank < 0 || rank > 256) return QL_E_ARG;
+    if (rank > 0 && (!mat1 || !mat2)) return QL_E_ARG;
+    if (stochastic != 0 && stochastic != 1) return QL_E_ARG;
+    if (!isfinite(alpha) || !isfinite(beta)) return QL_E_ARG;
+    if (!aligned(packed_w, 16) || !aligned(packed_s, 16)) return QL_E_ALIGN;
+    if (rank > 0 && (!aligned(mat1, 2) || !aligned(mat2, 2))) return QL_E_ALIGN;
+    const Layout L = layout_of(QL_INT8, N, K, group, 0);
+    return from_hip(launch_lora_merge8(L, packed_w, packed_s, mat1, mat2, int(rank), alpha, beta, stochastic, seed,
+                                       (hipStream_t)stream));
+}
+
 ql_status qlinear_unpack(ql_format f, int64_t N, int64_t K, int group, int has_zeros, const void *packed_w,
                          const void *packed_s, const void *packed_aux, void *codes, void *scales, void *aux_out,
                          void *stream) {

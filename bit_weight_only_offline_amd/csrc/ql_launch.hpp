@@ -16,6 +16,8 @@ hipError_t launch_dequant_tile(const Layout &L, const void *pw, const void *ps, 
 
 hipError_t launch_quantize(int fmt, int64_t N, int64_t K, int group, bool zp, const float *w,
                            const float *levels_host, void *codes, void *scales, void *zeros, hipStream_t st);
+hipError_t launch_lora_merge8(const Layout &L, void *pw, void *ps, const void *mat1, const void *mat2, int rank,
+                              float alpha, float beta, int stochastic, uint64_t seed, hipStream_t st);
 
 // One translation unit per format family keeps the template instantiations apart.
 hipError_t launch_gemm_int4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);

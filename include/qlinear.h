@@ -147,6 +147,39 @@ ql_status qlinear_quantize(ql_format f, int64_t N, int64_t K, int group, const f
                            const float *levels, void *codes, void *scales, void *zeros, void *stream);
 
 /*
+ * In-place low-rank update of a packed INT8 weight, requantised into the same buffers
+ * (piper-kernels package description, "ConvRot INT8": addmm_ computes
+ * weight = beta * weight + alpha * (mat1 @ mat2) with the Tensor.addmm_ contract,
+ * requantises and keeps the quantised storage; an unsigned 64-bit rounding seed picks
+ * one of the two neighbouring INT8 codes at random with probability set by the distance,
+ * without changing the deterministic scales; without a seed, nearest rounding).
+ * Every operation is IEEE float32 with one rounding:
+ *   w_old = q * s;  d_0 = +0,  d_j = fma(mat1[n, j], mat2[j, k], d_{j-1}) in index order
+ *   w = beta * w_old + alpha * d       (the two products rounded, then their sum)
+ *   s' = bf16(amax |w| / 127) per group   (the quantiser's INT8 rule, both modes)
+ *   v = w / s';  stochastic = 0: code = clamp(rint(v), -127, 127)
+ *                stochastic = 1: code = clamp(floor(v) + [u < v - floor(v)], -127, 127),
+ *                u = (SplitMix64 output n*K + k of `seed`) >> 40, times 2^-24
+ *   (SplitMix64, Steele, Lea and Flood 2014: output i = the 64-bit finaliser of
+ *   seed + (i + 1) * 0x9E3779B97F4A7C15).  A scale that rounds to zero gives codes 0.
+ *   N, K, group        as packed by qlinear_pack() (INT8)
+ *   packed_w, packed_s the weight's device buffers, read and rewritten in place (16-byte
+ *                      aligned); padding bytes keep their packed values
+ *   mat1               bf16 [N, rank] row-major (device): the adapter's B
+ *   mat2               bf16 [rank, K] row-major (device): the adapter's A
+ *   rank               0 .. 256 (0: mat1 and mat2 may be NULL; the update is then
+ *                      beta * W, requantised)
+ *   alpha, beta        finite
+ * Repeated updates are lossy, as the page warns: each one requantises.  Two updates of
+ * one weight must be ordered (one stream); the merged values must stay finite.
+ * Errors: QL_E_SHAPE as for qlinear_pack; QL_E_ARG for null buffers, a rank outside
+ * 0 .. 256, stochastic not 0 or 1, or non-finite alpha or beta; QL_E_ALIGN.
+ */
+ql_status qlinear_int8_addmm(int64_t N, int64_t K, int group, void *packed_w, void *packed_s,
+                             const void *mat1, const void *mat2, int64_t rank, float alpha, float beta,
+                             int stochastic, uint64_t seed, void *stream);
+
+/*
  * Inverse of qlinear_pack(): device layout -> canonical arrays, bit-exact.
  *   codes, scales   canonical outputs
  *   aux_out         INT4 with zeros: zeros [N, K/G]; CB4: float32 centroids [16]

@@ -51,6 +51,15 @@ Readings where the pages are silent (each also listed in the design notes):
   activation is materialised in the activation dtype before the linear.
 * Bias is bf16 [N], added before the final rounding; the reference output is the
   exact float64 Y, from which the bf16 output is one rounding away.
+* INT8 low-rank merge (piper-kernels, "ConvRot INT8", ``addmm_``): W <- beta W +
+  alpha (mat1 @ mat2), then requantised.  mat1 [N, r] and mat2 [r, K] are bf16; the
+  product's inner sum runs in index order as float32 fused multiply-adds (each step
+  d <- fp32(d + a*b) with the exact product, one rounding), then beta*W and
+  alpha*(mat1 @ mat2) are rounded to float32 and summed with one more rounding.  The group scales are
+  recomputed by the deterministic RTN rule above; without a seed the codes are RTN, with
+  a 64-bit seed each value v = w/s takes floor(v) + 1 with probability v - floor(v)
+  (the distance to floor(v)), else floor(v), by comparing that distance with a 24-bit
+  uniform drawn from SplitMix64 at counter n*K + k.
 """
 from __future__ import annotations
 
@@ -449,3 +458,91 @@ def canonical_bytes(fmt: str, N: int, K: int, group: int = 128, zeros: bool = Fa
     if fmt == "int8":
         return dict(codes=N * K, scales=2 * N * (K // group), aux=0)
     raise ValueError(fmt)
+
+
+# --------------------------------------------------------------------------------------
+# In-place low-rank update of an INT8 weight with requantisation
+# (piper-kernels package description, "ConvRot INT8": ``addmm_`` and ``rounding_seed``)
+# --------------------------------------------------------------------------------------
+
+SPLITMIX64_GAMMA = 0x9E3779B97F4A7C15
+
+
+def splitmix64(seed, index) -> np.ndarray:
+    """Output number ``index`` (0-based) of the SplitMix64 generator seeded with ``seed``.
+
+    SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+    OOPSLA 2014) walks a 64-bit state by the odd constant 0x9E3779B97F4A7C15 (the golden
+    ratio times 2^64) and sends each state through a 64-bit finaliser: xor-shift by 30,
+    multiply by 0xBF58476D1CE4E5B9, xor-shift by 27, multiply by 0x94D049BB133111EB,
+    xor-shift by 31 (Stafford's variant 13 of the MurmurHash3 finaliser).  Output i is
+    the finaliser of seed + (i + 1) * gamma, all modulo 2^64, so any output can be had
+    directly from its counter."""
+    with np.errstate(over="ignore"):
+        x = np.asarray(seed, dtype=np.uint64) + (np.asarray(index, dtype=np.uint64) + np.uint64(1)) * \
+            np.uint64(SPLITMIX64_GAMMA)
+        z = (x ^ (x >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        return z ^ (z >> np.uint64(31))
+
+
+def uniform24(seed, index) -> np.ndarray:
+    """The top 24 bits of SplitMix64 output ``index`` as a float32 in [0, 1) (exact)."""
+    return (splitmix64(seed, index) >> np.uint64(40)).astype(np.float32) * np.float32(2.0 ** -24)
+
+
+def lowrank_product_f32(mat1, mat2) -> np.ndarray:
+    """mat1 @ mat2 (bf16 operands) as a chain of float32 fused multiply-adds in index
+    order: d_0 = +0, d_j = fp32(d_{j-1} + mat1[:, j] * mat2[j, :]) with the product exact
+    and one rounding per step.
+
+    The product of two bf16 values (8 significant bits each) is exact in float64, and
+    so is nothing lost by first rounding d + a*b to float64: rounding a sum of two
+    operands of at most 24 significant bits to 53 bits and then to 24 bits gives the
+    single rounding to 24 bits (double rounding is innocuous when the first precision
+    has at least 2p + 1 bits; S. A. Figueroa, "When is double rounding innocuous?",
+    SIGNUM Newsletter 30(3), 1995)."""
+    m1 = np.asarray(mat1, dtype=np.float32).astype(np.float64)
+    m2 = np.asarray(mat2, dtype=np.float32).astype(np.float64)
+    d = np.zeros((m1.shape[0], m2.shape[1]), dtype=np.float32)
+    for j in range(m2.shape[0]):
+        d = (d.astype(np.float64) + m1[:, j:j + 1] * m2[j:j + 1, :]).astype(np.float32)
+    return d
+
+
+def merge_lowrank_int8(canon: dict, mat1, mat2, alpha=1.0, beta=1.0, seed=None, rows=None) -> dict:
+    """INT8 ``addmm_``: W <- beta * D(W) + alpha * (mat1 @ mat2), requantised to INT8 with
+    the same group size (piper-kernels, "ConvRot INT8": the update follows the standard
+    ``Tensor.addmm_`` contract and requantises; an unsigned 64-bit ``rounding_seed``
+    picks one of the two neighbouring INT8 codes at random with probability given by the
+    distance, keeps the deterministic scales and draws from no global generator; no seed
+    keeps nearest rounding).
+
+    canon: int8 canonical weight (codes int8 [N,K], scales bf16 bits [N,K/G]).
+    mat1: bf16-valued [N, r] (the adapter's B); mat2: bf16-valued [r, K] (its A).
+    rows: optional row subset (the result then holds only those rows, in that order).
+    The random draw for weight (n, k) is ``uniform24(seed, n*K + k)``; the upper code is
+    taken when that uniform is below v - floor(v)."""
+    G = int(canon["group"])
+    codes = np.asarray(canon["codes"], dtype=np.int8)
+    N, K = codes.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    w_old = dequant_int8(codes[rows], bf16_from_bits(np.asarray(canon["scales"])[rows]), G)
+    d = lowrank_product_f32(np.asarray(mat1, dtype=np.float32)[rows], mat2)
+    w = np.float32(beta) * w_old + np.float32(alpha) * d          # float32, three roundings
+    if seed is None:
+        q, s = quantize_int8(w, G)
+        return dict(codes=q, scales=bf16_bits(s), group=G)
+    wg = _groups(w, G)
+    amax = np.max(np.abs(wg), axis=2)
+    s = bf16_round(amax / np.float32(127.0))                       # the deterministic scale
+    ok = s > 0
+    sd = np.where(ok, s, np.float32(1))[..., None]
+    v = wg / sd
+    lo = np.floor(v)
+    dist = v - lo                                                 # exact in float32
+    ctr = rows[:, None].astype(np.uint64) * np.uint64(K) + np.arange(K, dtype=np.uint64)[None, :]
+    u = uniform24(seed, ctr).reshape(wg.shape)
+    q = lo + (u < dist)
+    q = np.where(ok[..., None], np.clip(q, -127, 127), 0)
+    return dict(codes=q.astype(np.int8).reshape(w.shape), scales=bf16_bits(s), group=G)

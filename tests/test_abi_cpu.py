@@ -223,3 +223,18 @@ def test_schedule_entry_points(L):
     assert L.qlinear_workspace_bytes_ex(INT4, 17, 4096, 4096, 128, 0, ctypes.byref(dec), ctypes.byref(b)) == 4
     dec2 = Sched(0, 2)
     assert L.qlinear_workspace_bytes_ex(INT4, 8, 4096, 4096, 128, 0, ctypes.byref(dec2), ctypes.byref(b)) == 4
+
+
+def test_int8_addmm_validation_before_launch(L):
+    def a(N=64, K=256, G=256, w=FAKE, s=FAKE, m1=FAKE, m2=FAKE, r=8, alpha=1.0, beta=1.0, st=0, seed=0):
+        return L.qlinear_int8_addmm(N, K, G, w, s, m1, m2, r, ctypes.c_float(alpha), ctypes.c_float(beta), st,
+                                    ctypes.c_uint64(seed), None)
+
+    assert a(G=100) == QL_E_SHAPE and a(K=250) == QL_E_SHAPE and a(K=128) == QL_E_SHAPE   # K % group
+    assert a(N=0) == QL_E_SHAPE
+    assert a(w=None) == QL_E_ARG and a(s=None) == QL_E_ARG
+    assert a(m1=None) == QL_E_ARG and a(m2=None) == QL_E_ARG
+    assert a(r=-1) == QL_E_ARG and a(r=257) == QL_E_ARG
+    assert a(st=2) == QL_E_ARG
+    assert a(alpha=float("nan")) == QL_E_ARG and a(beta=float("inf")) == QL_E_ARG
+    assert a(w=FAKE + 8) == QL_E_ALIGN and a(s=FAKE + 4) == QL_E_ALIGN and a(m1=FAKE + 1) == QL_E_ALIGN

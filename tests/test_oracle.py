@@ -403,3 +403,189 @@ def test_synthetic_workloads_shapes_and_outliers():
     x = S.activations(S.WORKLOADS["int8_swiglu"], 1, K=64)
     assert x.shape == (1, 128)
     assert np.array_equal(O.bf16_round(x), x)
+
+
+# ------------------------------------------------- INT8 low-rank merge (addmm_) and its RNG
+
+def test_splitmix64_known_answers():
+    rows = {r[0]: r[1:] for r in _golden("splitmix64.txt")}
+    seed, *vals = rows["first5"]
+    got = O.splitmix64(int(seed), np.arange(5))
+    assert [int(v) for v in got] == [int(v) for v in vals]
+    seed, *counts = rows["buckets5"]
+    z = O.splitmix64(int(seed), np.arange(100000))
+    buckets = [(int(v) * 5) >> 64 for v in z]
+    assert list(np.bincount(buckets, minlength=5)) == [int(c) for c in counts]
+
+
+def test_uniform24_is_the_top_bits():
+    z = O.splitmix64(99, np.arange(1000))
+    u = O.uniform24(99, np.arange(1000))
+    assert u.dtype == np.float32
+    assert np.all((u >= 0) & (u < 1))
+    assert all(Fraction(float(a)) == Fraction(int(b) >> 40, 1 << 24) for a, b in zip(u, z))
+
+
+def _int8_canon(rng, N, K, G):
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    return O.quantize("int8", w, G)
+
+
+def test_merge_identity_when_alpha_is_zero():
+    """beta = 1, alpha = 0 requantises D(W) itself: every RTN group holds a code of
+    magnitude 127, so the scale and every code come back unchanged, in both modes."""
+    rng = np.random.default_rng(0)
+    for G in (32, 64, 256):
+        c = _int8_canon(rng, 5, 512, G)
+        m1 = S.to_bf16_values(rng.standard_normal((5, 4)).astype(np.float32))
+        m2 = S.to_bf16_values(rng.standard_normal((4, 512)).astype(np.float32))
+        for seed in (None, 0, 2 ** 64 - 1):
+            out = O.merge_lowrank_int8(c, m1, m2, alpha=0.0, beta=1.0, seed=seed)
+            assert np.array_equal(out["codes"], c["codes"]) and np.array_equal(out["scales"], c["scales"])
+
+
+def _exact_fixture(rng, N, K, G, r, beta):
+    """Dyadic inputs whose float32 merge is exact and whose new scale is a power of two:
+    old scales 2^-5, codes |q| <= 100 except one planted +-127 per group at a k where
+    mat2 is zero, mat1 and mat2 in quarter steps.  Then amax = 127 * beta / 32 exactly
+    and s' = beta / 32."""
+    q = rng.integers(-100, 101, (N, K)).astype(np.int8)
+    m2 = (rng.integers(-2, 3, (r, K)) / 4.0).astype(np.float32)
+    for g in range(K // G):
+        q[:, g * G] = rng.choice([-127, 127], N)
+        m2[:, g * G] = 0.0
+    m1 = (rng.integers(-2, 3, (N, r)) / 4.0).astype(np.float32)
+    scales = O.bf16_bits(np.full((N, K // G), 2.0 ** -5, np.float32))
+    return dict(codes=q, scales=scales, group=G), m1, m2
+
+
+def _brute_merge(canon, m1, m2, alpha, beta, seed):
+    """The merge in exact rational arithmetic, codes by exhaustive search over -127..127."""
+    q, G = canon["codes"], canon["group"]
+    N, K = q.shape
+    r = m1.shape[1]
+    s_old = Fraction(2) ** -5
+    codes = np.zeros((N, K), np.int8)
+    scales = np.zeros((N, K // G), np.float64)
+    cand = list(range(-127, 128))
+    for n in range(N):
+        for g in range(K // G):
+            ks = range(g * G, (g + 1) * G)
+            w = {}
+            for k in ks:
+                d = sum(Fraction(float(m1[n, j])) * Fraction(float(m2[j, k])) for j in range(r))
+                w[k] = Fraction(beta) * int(q[n, k]) * s_old + Fraction(alpha) * d
+            amax = max(abs(v) for v in w.values())
+            s = amax / 127
+            scales[n, g] = float(s)
+            for k in ks:
+                if seed is None:
+                    best = min(abs(w[k] - c * s) for c in cand)
+                    ties = [c for c in cand if abs(w[k] - c * s) == best]
+                    codes[n, k] = [c for c in ties if c % 2 == 0][0] if len(ties) > 1 else ties[0]
+                else:
+                    lo = max(c for c in cand if c * s <= w[k])
+                    dist = w[k] / s - lo
+                    u = Fraction(int(O.splitmix64(seed, n * K + k)) >> 40, 1 << 24)
+                    codes[n, k] = min(lo + 1, 127) if u < dist else lo
+    return codes, scales
+
+
+@pytest.mark.parametrize("beta,alpha,seed", [(1.0, 0.25, None), (0.5, -0.125, None), (1.0, 0.25, 7),
+                                             (0.5, 0.375, 2 ** 63 + 5)])
+def test_merge_against_exact_rationals(beta, alpha, seed):
+    rng = np.random.default_rng(int(beta * 8) + (seed or 0) % 97)
+    N, K, G, r = 3, 64, 32, 3
+    canon, m1, m2 = _exact_fixture(rng, N, K, G, r, beta)
+    out = O.merge_lowrank_int8(canon, m1, m2, alpha=alpha, beta=beta, seed=seed)
+    codes, scales = _brute_merge(canon, m1, m2, alpha, beta, seed)
+    assert np.array_equal(O.bf16_from_bits(out["scales"]).astype(np.float64), scales)
+    assert np.array_equal(out["codes"], codes)
+    # the fixture must reach rounding ties (nearest) or fractional distances (stochastic)
+    if seed is not None:
+        assert not np.array_equal(out["codes"], O.merge_lowrank_int8(canon, m1, m2, alpha=alpha, beta=beta)["codes"])
+
+
+def test_merge_stochastic_is_unbiased_and_picks_neighbours():
+    """Over many seeds the mean code is w / s' (the draw is unbiased), every code is one
+    of the two neighbours of w / s', and a larger distance means the upper code more
+    often."""
+    rng = np.random.default_rng(3)
+    N, K, G, r = 4, 256, 64, 8
+    c = _int8_canon(rng, N, K, G)
+    m1 = S.to_bf16_values((rng.standard_normal((N, r)) * 0.05).astype(np.float32))
+    m2 = S.to_bf16_values((rng.standard_normal((r, K)) * 0.05).astype(np.float32))
+    det = O.merge_lowrank_int8(c, m1, m2, alpha=0.7, beta=0.9)
+    s = np.repeat(O.bf16_from_bits(det["scales"]), G, axis=1).astype(np.float64)
+    w = 0.9 * O.dequant("int8", c, K).astype(np.float64) + 0.7 * (m1.astype(np.float64) @ m2.astype(np.float64))
+    v = w / s
+    draws = np.stack([O.merge_lowrank_int8(c, m1, m2, alpha=0.7, beta=0.9, seed=sd)["codes"] for sd in range(300)])
+    inside = np.abs(v) <= 127            # beyond +-127 (a group's amax, when bf16 rounded
+    assert np.all((draws == np.floor(v)) | (draws == np.floor(v) + 1) | ~inside)   # s' down) clamps
+    assert np.all(np.abs(draws[:, ~inside]) == 127)
+    mean = draws.astype(np.float64).mean(axis=0)
+    assert np.max(np.abs(mean - v)[inside]) < 6 * 0.5 / np.sqrt(300)
+    frac = (v - np.floor(v))[inside]
+    up = (draws == np.floor(v) + 1).mean(axis=0)[inside]
+    assert np.corrcoef(frac, up)[0, 1] > 0.95
+    # the scales are the deterministic ones in every draw
+    assert all(np.array_equal(O.merge_lowrank_int8(c, m1, m2, 0.7, 0.9, seed=sd)["scales"], det["scales"])
+               for sd in (1, 2))
+
+
+def test_merge_rows_subset_matches_full():
+    rng = np.random.default_rng(4)
+    c = _int8_canon(rng, 9, 128, 32)
+    m1 = S.to_bf16_values(rng.standard_normal((9, 5)).astype(np.float32) * 0.01)
+    m2 = S.to_bf16_values(rng.standard_normal((5, 128)).astype(np.float32))
+    full = O.merge_lowrank_int8(c, m1, m2, 1.5, 1.0, seed=11)
+    rows = np.array([7, 0, 4])
+    part = O.merge_lowrank_int8(c, m1, m2, 1.5, 1.0, seed=11, rows=rows)
+    assert np.array_equal(part["codes"], full["codes"][rows]) and np.array_equal(part["scales"], full["scales"][rows])
+
+
+def _rn32(x: Fraction) -> float:
+    """Round a rational to the nearest float32 (ties to even), subnormals included."""
+    if x == 0:
+        return 0.0
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()      # 2^(e-1) <= a < 2^(e+1)
+    if Fraction(2) ** e > a:
+        e -= 1
+    q = Fraction(2) ** (max(e, -126) - 23)                           # spacing of float32 at a
+    m = a / q
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return float(n * q) if x > 0 else -float(n * q)
+
+
+def test_lowrank_product_is_a_chain_of_fused_multiply_adds():
+    """d_j = fp32(d_{j-1} + a_j b_j) with the exact product, checked against exact rational
+    arithmetic and a correct rounding to float32; the operands reach products far below
+    the float32 normal range, where a separately rounded product would differ."""
+    rng = np.random.default_rng(12)
+    R, C, r = 6, 40, 7
+
+    def bf16_vals(shape, lo, hi):
+        mant = 1 + rng.integers(0, 128, shape) / 128.0
+        ex = rng.integers(lo, hi, shape)
+        sign = np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+        return (sign * mant * np.exp2(ex)).astype(np.float32)
+
+    m1, m2 = bf16_vals((R, r), -75, 6), bf16_vals((r, C), -75, 6)
+    m1[:2] = bf16_vals((2, r), -76, -68)           # products near and below 2^-140, where
+    m2[:, :12] = bf16_vals((r, 12), -76, -68)      # float32 is subnormal (spacing 2^-149)
+    assert np.array_equal(S.to_bf16_values(m1), m1) and np.array_equal(S.to_bf16_values(m2), m2)
+    got = O.lowrank_product_f32(m1, m2)
+    for i in range(R):
+        for k in range(C):
+            d = 0.0
+            for j in range(r):
+                d = _rn32(Fraction(d) + Fraction(float(m1[i, j])) * Fraction(float(m2[j, k])))
+            assert np.float32(d).view(np.uint32) == got[i, k].view(np.uint32), (i, k)
+    sep = np.zeros((R, C), np.float32)
+    for j in range(r):
+        sep = sep + m1[:, j:j + 1] * m2[j:j + 1, :]
+    assert not np.array_equal(sep, got)          # the fixture tells the two semantics apart
