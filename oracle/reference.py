@@ -60,6 +60,10 @@ Readings where the pages are silent (each also listed in the design notes):
   a 64-bit seed each value v = w/s takes floor(v) + 1 with probability v - floor(v)
   (the distance to floor(v)), else floor(v), by comparing that distance with a 24-bit
   uniform drawn from SplitMix64 at counter n*K + k.
+* INT8-compute path (AutoRound Kernel, "1. Linear": W4A8 / W8A8 with dynamic activation
+  quantisation, QQQ-style): each activation row is quantised symmetrically with its own
+  float32 scale s_m = amax_m / 127 and codes clamp(rint(x / s_m), -127, 127); the output
+  is the exact product of those dequantised activations with D(Wq).
 """
 from __future__ import annotations
 
@@ -546,3 +550,32 @@ def merge_lowrank_int8(canon: dict, mat1, mat2, alpha=1.0, beta=1.0, seed=None, 
     q = lo + (u < dist)
     q = np.where(ok[..., None], np.clip(q, -127, 127), 0)
     return dict(codes=q.astype(np.int8).reshape(w.shape), scales=bf16_bits(s), group=G)
+
+
+# --------------------------------------------------------------------------------------
+# INT8-compute variant: dynamic per-token activation quantisation
+# (AutoRound Kernel package description, "1. Linear": "Key Features" W4A8 rescale,
+# QQQ-style; "Supported Data Types" note: INT8 compute includes dynamic activation
+# quantisation and results are dequantised to floating point)
+# --------------------------------------------------------------------------------------
+
+
+def quantize_activations_int8(x):
+    """Per-row symmetric INT8 quantisation of activations [M, K] in float32:
+    s_m = fp32(amax_m / 127), q = clamp(rint(x / s_m), -127, 127) (ties to even);
+    an all-zero row gets s = 0 and codes 0.  -> (codes int8 [M, K], scales float32 [M])."""
+    a = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(a), axis=1) if a.shape[1] else np.zeros(a.shape[0], np.float32)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    ok = s > 0
+    sd = np.where(ok, s, np.float32(1))[:, None]
+    q = np.where(ok[:, None], np.clip(np.rint(a / sd), -127, 127), 0)
+    return q.astype(np.int8), s
+
+
+def forward_a8(fmt: str, x, canon: dict, K: int, bias=None) -> np.ndarray:
+    """Exact output (float64) of the INT8-compute linear: the activation rows quantised by
+    ``quantize_activations_int8`` and dequantised (codes times row scale), times D(Wq)."""
+    q, s = quantize_activations_int8(x)
+    a = q.astype(np.float64) * s.astype(np.float64)[:, None]
+    return linear_ref(a, dequant(fmt, canon, K), bias)

@@ -589,3 +589,54 @@ def test_lowrank_product_is_a_chain_of_fused_multiply_adds():
     for j in range(r):
         sep = sep + m1[:, j:j + 1] * m2[j:j + 1, :]
     assert not np.array_equal(sep, got)          # the fixture tells the two semantics apart
+
+
+# ------------------------------------------- INT8-compute path: activation quantisation
+
+def test_activation_quant_on_grid_ties_and_zero_rows():
+    rng = np.random.default_rng(20)
+    K = 96
+    q = rng.integers(-127, 128, (4, K))
+    q[:, 5] = 127
+    q[1, 9] = -127
+    x_grid = (q * 2.0 ** -3).astype(np.float32)                     # s = 2^-3 exactly
+    t = rng.integers(-126, 126, (3, K)).astype(np.float64) + 0.5
+    t[:, 0] = 127.0
+    x_tie = (t * 2.0 ** -4).astype(np.float32)                      # every other value a rint tie
+    x = np.vstack([x_grid, x_tie, np.zeros((1, K), np.float32)])
+    assert np.array_equal(S.to_bf16_values(x), x)                   # bf16 activations
+    codes, s = O.quantize_activations_int8(x)
+    assert np.array_equal(s[:4], np.full(4, 0.125, np.float32)) and np.array_equal(codes[:4], q)
+    assert np.array_equal(s[4:7], np.full(3, 2.0 ** -4, np.float32))
+    lo = np.floor(t)
+    even = np.where(lo % 2 == 0, lo, lo + 1)                        # ties to the even code
+    assert np.array_equal(codes[4:7], np.where(t == np.rint(t), t, even).astype(np.int8))
+    assert s[7] == 0 and not codes[7].any()
+
+
+def test_activation_quant_error_bound():
+    rng = np.random.default_rng(21)
+    x = S.to_bf16_values(rng.standard_normal((16, 512)).astype(np.float32) * np.exp2(rng.integers(-20, 20, (16, 1))))
+    codes, s = O.quantize_activations_int8(x)
+    assert np.array_equal(s, (np.abs(x).max(axis=1) / np.float32(127)).astype(np.float32))
+    err = np.abs(x.astype(np.float64) - codes.astype(np.float64) * s[:, None])
+    assert np.all(err <= s[:, None] * (0.5 + 128 * 2.0 ** -23))     # + the rounding of x / s
+    assert np.all(np.abs(codes).max(axis=1) == 127)
+
+
+@pytest.mark.parametrize("fmt,G", [("int4", 64), ("int8", 128)])
+def test_forward_a8_exact_rationals(fmt, G):
+    rng = np.random.default_rng(22)
+    M, N, K = 3, 4, 256
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    canon = O.quantize(fmt, w, G, symmetric=True)
+    x = S.to_bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    b = S.to_bf16_values(rng.standard_normal(N).astype(np.float32) * 0.01)
+    y = O.forward_a8(fmt, x, canon, K, b)
+    codes, s = O.quantize_activations_int8(x)
+    dw = O.dequant(fmt, canon, K)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(int(codes[m, k])) * Fraction(float(s[m])) * Fraction(float(dw[n, k]))
+                        for k in range(K)) + Fraction(float(b[n]))
+            assert abs(Fraction(float(y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
