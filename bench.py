@@ -18,7 +18,8 @@ Also reported, on the same line:
            sample of the same workload, on the host cores
   sweep    (--sweep) the decode workload at M = 1, 4, 8, the other workloads, the grouped
            (mixture-of-experts) linear, the on-device quantiser (float32 weights in,
-           canonical codes out) and the in-place INT8 low-rank merge
+           canonical codes out), the in-place INT8 low-rank merge and the INT8-compute
+           (W4A8 / W8A8) linear
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--sweep]
 Profiling helpers (used to write the summaries kept with the benchmark):
@@ -471,6 +472,32 @@ def main():
             del wd
             torch.cuda.empty_cache()
 
+    a8 = {}
+    if args.sweep:
+        # INT8-compute path (W4A8 / W8A8) at the prefill shape 3072 x 3072: default
+        # schedule, activation quantisation included, weights from HBM
+        for fmt_, G_ in (("int4", 128), ("int8", 128)):
+            pl = _pool(Q, fmt_, 3072, 3072, G_, True, 17, POOL_BYTES)
+            for M in (256, 2048):
+                xa = torch.randn(M, 3072, device="cuda").to(torch.bfloat16)
+                outa = torch.empty(M, 3072, device="cuda", dtype=torch.bfloat16)
+                wsa = torch.empty(Q.a8_workspace_bytes(fmt_, M, 3072, 3072, G_) + 256, dtype=torch.uint8,
+                                  device="cuda")
+                for i in range(3):
+                    Q.linear_a8(xa, pl[i % len(pl)], out=outa, workspace=wsa)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(40):
+                    Q.linear_a8(xa, pl[i % len(pl)], out=outa, workspace=wsa)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 40
+                a8[f"{fmt_}_g{G_}_3072/M{M}"] = {"us": round(ms * 1e3, 2),
+                                                 "TOPS": round(2.0 * M * 3072 * 3072 / (ms * 1e-3) / 1e12, 1)}
+            del pl
+            torch.cuda.empty_cache()
+
     merge = {}
     if args.sweep:
         # in-place INT8 low-rank merge on the INT8 SwiGLU layer's weight (8192 x 28672,
@@ -533,6 +560,8 @@ def main():
         rec["quantize"] = quant
     if merge:
         rec["int8_merge"] = merge
+    if a8:
+        rec["int8_compute"] = a8
     if moe:
         rec["moe"] = moe
     print(json.dumps(rec), flush=True)

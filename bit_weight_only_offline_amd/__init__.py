@@ -18,7 +18,8 @@ __all__ = [
     "QL_INT4", "QL_MXFP4", "QL_INT8", "QL_CB4", "FORMATS", "QLinearError", "lib", "version",
     "PackedWeight", "packed_bytes", "quantize", "pack", "unpack", "dequant_tile", "workspace_bytes", "linear",
     "Schedule", "default_schedule", "tile_shapes", "workspace", "PackedExperts", "pack_experts",
-    "grouped_workspace_bytes", "grouped_linear", "int8_addmm_",
+    "grouped_workspace_bytes", "grouped_linear", "int8_addmm_", "quantize_activations", "a8_tile_shapes",
+    "a8_workspace_bytes", "linear_a8",
 ]
 
 QL_INT4, QL_MXFP4, QL_INT8, QL_CB4 = 0, 1, 2, 3
@@ -60,6 +61,15 @@ def lib() -> ctypes.CDLL:
         L.qlinear_grouped_forward.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, vp, ci, ci, ci, vp, vp, ci, vp, sz, vp]
         L.qlinear_quantize.restype = ci
         L.qlinear_int8_addmm.restype = ci
+        L.qlinear_quantize_activations.restype = ci
+        L.qlinear_quantize_activations.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.qlinear_a8_workspace_bytes.restype = ci
+        L.qlinear_a8_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(sz)]
+        L.qlinear_a8_num_tiles.restype = ci
+        L.qlinear_a8_tile_shape.restype = ci
+        L.qlinear_a8_tile_shape.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
+        L.qlinear_forward_a8.restype = ci
+        L.qlinear_forward_a8.argtypes = [vp, i64, i64, i64, vp, vp, ci, ci, vp, vp, ci, vp, sz, ci, vp]
         L.qlinear_int8_addmm.argtypes = [i64, i64, ci, vp, vp, vp, vp, i64, ctypes.c_float, ctypes.c_float, ci,
                                          ctypes.c_uint64, vp]
         L.qlinear_quantize.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp, vp, vp]
@@ -469,3 +479,72 @@ def grouped_linear(x: torch.Tensor, pe: PackedExperts, tokens_per_expert: torch.
                                          _stream(x.device)), "qlinear_grouped_forward")
     return out
 
+
+
+# ---- INT8-compute path (W4A8 / W8A8): dynamic per-row activation quantisation ----------
+
+def quantize_activations(x: torch.Tensor):
+    """Per-row symmetric INT8 quantisation of bf16 activations [M, K]:
+    -> (codes int8 [M, K], scales float32 [M]), s = amax / 127, q = rint(x / s)."""
+    if x.requires_grad:
+        raise QLinearError("inference-only operator: inputs must not require grad")
+    if x.device.type != "cuda" or x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise QLinearError("x must be a bf16 [M, K] device tensor")
+    x = x.contiguous()
+    M, K = x.shape
+    codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().qlinear_quantize_activations(_ptr(x), M, K, _ptr(codes), _ptr(scales), _stream(x.device)),
+           "qlinear_quantize_activations")
+    return codes, scales
+
+
+def a8_tile_shapes():
+    """[(rows, cols)] of the INT8-compute kernel's compiled schedules."""
+    out = []
+    for t in range(lib().qlinear_a8_num_tiles()):
+        r, c = ctypes.c_int(), ctypes.c_int()
+        _check(lib().qlinear_a8_tile_shape(t, ctypes.byref(r), ctypes.byref(c)), "qlinear_a8_tile_shape")
+        out.append((r.value, c.value))
+    return out
+
+
+def a8_workspace_bytes(fmt, M: int, N: int, K: int, group: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().qlinear_a8_workspace_bytes(_fmt(fmt), M, N, K, group, ctypes.byref(n)), "qlinear_a8_workspace_bytes")
+    return n.value
+
+
+def linear_a8(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, tile: int | None = None):
+    """Y = dequant(quantise_int8(x)) . D(W)^T + bias on the INT8 matrix cores, for symmetric
+    INT4 or INT8 packed weights (group >= 64).  x bf16 [..., K]; tile None = automatic."""
+    if x.requires_grad or (bias is not None and bias.requires_grad):
+        raise QLinearError("inference-only operator: inputs must not require grad")
+    if x.device.type != "cuda" or x.dtype != torch.bfloat16:
+        raise QLinearError("x must be a bf16 device tensor")
+    if x.shape[-1] != pw.K:
+        raise QLinearError(f"x has {x.shape[-1]} inputs, the weight {pw.K}")
+    if pw.has_zeros:
+        raise QLinearError("the INT8-compute path takes symmetric weights")
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, pw.K).contiguous()
+    M = x2.shape[0]
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise QLinearError("out_dtype must be bf16 or float32")
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=out_dtype, device=x.device)
+    elif out.dtype != out_dtype or out.numel() != M * pw.N or not out.is_contiguous():
+        raise QLinearError("out must be a contiguous [M, N] tensor of out_dtype")
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or bias.numel() != pw.N:
+            raise QLinearError("bias must be bf16 [N]")
+        bias = bias.contiguous()
+    need = a8_workspace_bytes(pw.fmt, M, pw.N, pw.K, pw.group)
+    if workspace is None:
+        workspace = _shared_workspace(x.device, need)
+    od = 1 if out_dtype == torch.float32 else 0
+    _check(lib().qlinear_forward_a8(_ptr(x2), M, pw.N, pw.K, _ptr(pw.w), _ptr(pw.s), pw.fmt, pw.group, _ptr(bias),
+                                    _ptr(out), od, _ptr(workspace), workspace.numel(),
+                                    -1 if tile is None else int(tile), _stream(x.device)), "qlinear_forward_a8")
+    return out.reshape(*lead, pw.N)

@@ -27,6 +27,7 @@ SOURCES = [
     "ql_misc.hip",
     "ql_quant.hip",
     "ql_lora.hip",
+    "ql_gemm_a8.hip",
 ]
 
 ARCH = "gfx950"

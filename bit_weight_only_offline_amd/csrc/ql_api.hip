@@ -136,6 +136,62 @@ ql_status qlinear_int8_addmm(int64_t N, int64_t K, int group, void *packed_w, vo
                                        (hipStream_t)stream));
 }
 
+ql_status qlinear_quantize_activations(const void *x, int64_t M, int64_t K, void *codes, float *scales,
+                                        void *stream) {
+    if (M < 0 || M >= (int64_t(1) << 31) || K <= 0 || K % 32 != 0 || K >= (int64_t(1) << 30)) return QL_E_SHAPE;
+    if (M == 0) return QL_OK;
+    if (!x || !codes || !scales) return QL_E_ARG;
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4)) return QL_E_ALIGN;
+    return from_hip(launch_quant_act(static_cast<const uint16_t *>(x), int(M), int(K), int(K), 0,
+                                     static_cast<int8_t *>(codes), scales, (hipStream_t)stream));
+}
+
+ql_status qlinear_a8_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, int group, size_t *bytes) {
+    if (!bytes) return QL_E_ARG;
+    if (f != QL_INT4 && f != QL_INT8) return QL_E_UNSUPPORTED;
+    ql_status st = check_format(f, N, K, group, 0);
+    if (st != QL_OK) return st;
+    if (group < 64) return QL_E_UNSUPPORTED;
+    if (M < 0 || M >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    const Layout L = layout_of(f, N, K, group, 0);
+    *bytes = M == 0 ? 0 : round256(size_t(M) * size_t(L.Kp)) + round256(size_t(M) * 4);
+    return QL_OK;
+}
+
+int qlinear_a8_num_tiles(void) { return NUM_A8_TILES; }
+
+ql_status qlinear_a8_tile_shape(int tile, int *rows, int *cols) {
+    if (tile < 0 || tile >= NUM_A8_TILES || !rows || !cols) return QL_E_ARG;
+    *rows = 16 * A8_TILES[tile].MT * A8_TILES[tile].WM;
+    *cols = 16 * A8_TILES[tile].NT * A8_TILES[tile].WN;
+    return QL_OK;
+}
+
+ql_status qlinear_forward_a8(const void *x, int64_t M, int64_t N, int64_t K, const void *packed_w,
+                             const void *packed_s, ql_format f, int group, const void *bias, void *out,
+                             ql_dtype out_dtype, void *workspace, size_t workspace_bytes, int tile, void *stream) {
+    size_t need = 0;
+    ql_status st = qlinear_a8_workspace_bytes(f, M, N, K, group, &need);
+    if (st != QL_OK) return st;
+    if (out_dtype != QL_BF16 && out_dtype != QL_F32) return QL_E_ARG;
+    if (tile < -1 || tile >= NUM_A8_TILES) return QL_E_ARG;
+    const Layout L = layout_of(f, N, K, group, 0);
+    // the quantised rows are addressed with 32-bit buffer offsets whose bit 31 marks
+    // "out of range"
+    if (M * L.Kp >= (int64_t(1) << 30) || M * N >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    if (M == 0) return QL_OK;
+    if (!x || !packed_w || !packed_s || !out) return QL_E_ARG;
+    if (!aligned(x, 16) || !aligned(packed_w, 16) || !aligned(packed_s, 16)) return QL_E_ALIGN;
+    if (bias && !aligned(bias, 2)) return QL_E_ALIGN;
+    if (!aligned(out, out_dtype == QL_F32 ? 4 : 2)) return QL_E_ALIGN;
+    if (!workspace || workspace_bytes < need) return QL_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return QL_E_ALIGN;
+    int8_t *xq = static_cast<int8_t *>(workspace);
+    float *xs = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + round256(size_t(M) * size_t(L.Kp)));
+    return from_hip(launch_gemm_a8(L, tile < 0 ? default_a8_tile(M) : tile, static_cast<const uint16_t *>(x), int(M),
+                                   packed_w, packed_s, bias, out, out_dtype == QL_F32, xq, xs, (hipStream_t)stream));
+}
+
 ql_status qlinear_unpack(ql_format f, int64_t N, int64_t K, int group, int has_zeros, const void *packed_w,
                          const void *packed_s, const void *packed_aux, void *codes, void *scales, void *aux_out,
                          void *stream) {

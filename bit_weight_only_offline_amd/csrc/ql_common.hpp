@@ -75,6 +75,17 @@ inline Layout make_layout(int fmt, int64_t N, int64_t K, int group, bool zeros) 
     return L;
 }
 
+// Schedules of the INT8-compute (W4A8 / W8A8) ring kernel: MT x NT 16x16 tiles per
+// wavefront, WM x WN wavefronts.
+struct A8Tile {
+    int MT, NT, WM, WN;
+};
+constexpr int NUM_A8_TILES = 5;
+constexpr A8Tile A8_TILES[NUM_A8_TILES] = {
+    {8, 3, 1, 4}, {4, 4, 2, 2}, {4, 4, 1, 4}, {2, 4, 1, 4}, {1, 4, 1, 4},
+};
+inline int default_a8_tile(int64_t M) { return M <= 16 ? 4 : (M <= 32 ? 3 : (M <= 64 ? 2 : 0)); }
+
 // Launch arguments of the linear kernels.
 struct GemmArgs {
     const uint16_t *x;     // bf16 activations, row stride ldx elements

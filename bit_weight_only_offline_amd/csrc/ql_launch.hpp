@@ -16,6 +16,10 @@ hipError_t launch_dequant_tile(const Layout &L, const void *pw, const void *ps, 
 
 hipError_t launch_quantize(int fmt, int64_t N, int64_t K, int group, bool zp, const float *w,
                            const float *levels_host, void *codes, void *scales, void *zeros, hipStream_t st);
+hipError_t launch_quant_act(const uint16_t *x, int M, int K, int Kp, int layout, int8_t *codes, float *scales,
+                            hipStream_t st);
+hipError_t launch_gemm_a8(const Layout &L, int tile, const uint16_t *x, int M, const void *pw, const void *ps,
+                          const void *bias, void *out, bool out_f32, int8_t *xq, float *xs, hipStream_t st);
 hipError_t launch_lora_merge8(const Layout &L, void *pw, void *ps, const void *mat1, const void *mat2, int rank,
                               float alpha, float beta, int stochastic, uint64_t seed, hipStream_t st);
 

@@ -278,6 +278,38 @@ ql_status qlinear_forward_ex(const void *x, int64_t M, int64_t N, int64_t K,
                              void *stream);
 
 /*
+ * INT8-compute variant (W4A8 / W8A8; AutoRound Kernel package description, "1. Linear":
+ * "Key Features", W4A8 / W2A8 rescale in the style of QQQ, low-bit weights re-scaled to
+ * INT8 and computed by an INT8 GEMM; "Supported Data Types": INT8 compute includes dynamic
+ * activation quantisation, results dequantised to floating point).
+ *
+ * qlinear_quantize_activations: per-row symmetric INT8 quantisation of bf16 activations,
+ * IEEE float32 with round-to-nearest-even: s_m = amax_m / 127,
+ * q = clamp(rint(x / s_m), -127, 127); an all-zero row gets s = 0 and codes 0.
+ *   x       bf16 [M, K] (device, 16-byte aligned), K a multiple of 32
+ *   codes   out: int8 [M, K] (8-byte aligned)      scales  out: float32 [M]
+ *
+ * qlinear_forward_a8: Y = (q * s) . D(Wq)^T + bias, with q and s as above, computed on
+ * the INT8 matrix cores: exact int32 sums per weight group, group scale and row scale
+ * in float32, then bias and the output rounding.  Weights: symmetric INT4 (no
+ * zero-points) or INT8, packed by qlinear_pack(), group 64, 128 or 256.
+ *   workspace   qlinear_a8_workspace_bytes() bytes, 256-byte aligned: the quantised
+ *               rows (in the kernel's input order) and their scales are written there
+ *   tile        -1: automatic; else 0 .. qlinear_a8_num_tiles() - 1
+ * Errors: QL_E_UNSUPPORTED for other formats, zero-points or group 32; otherwise as for
+ * qlinear_forward().  M = 0 is a no-op.
+ */
+ql_status qlinear_quantize_activations(const void *x, int64_t M, int64_t K, void *codes, float *scales,
+                                        void *stream);
+ql_status qlinear_a8_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, int group, size_t *bytes);
+int qlinear_a8_num_tiles(void);
+ql_status qlinear_a8_tile_shape(int tile, int *rows, int *cols);
+ql_status qlinear_forward_a8(const void *x, int64_t M, int64_t N, int64_t K, const void *packed_w,
+                             const void *packed_s, ql_format f, int group, const void *bias, void *out,
+                             ql_dtype out_dtype, void *workspace, size_t workspace_bytes, int tile,
+                             void *stream);
+
+/*
  * Grouped (mixture-of-experts) linear: every token is multiplied by its own expert's
  * packed weight (AutoRound Kernel package description, "2. MoE (Mixture-of-Experts Grouped
  * GEMM)": activations [total_tokens, K], per-expert weights, num_tokens_per_expert [E]

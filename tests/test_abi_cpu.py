@@ -238,3 +238,27 @@ def test_int8_addmm_validation_before_launch(L):
     assert a(st=2) == QL_E_ARG
     assert a(alpha=float("nan")) == QL_E_ARG and a(beta=float("inf")) == QL_E_ARG
     assert a(w=FAKE + 8) == QL_E_ALIGN and a(s=FAKE + 4) == QL_E_ALIGN and a(m1=FAKE + 1) == QL_E_ALIGN
+
+
+def test_a8_validation_before_launch(L):
+    need = ctypes.c_size_t()
+    assert L.qlinear_a8_workspace_bytes(INT4, 2048, 3072, 3072, 128, ctypes.byref(need)) == QL_OK
+    assert need.value == 2048 * 3072 + 2048 * 4
+    assert L.qlinear_a8_workspace_bytes(MXFP4, 16, 256, 256, 32, ctypes.byref(need)) == QL_E_UNSUPPORTED
+    assert L.qlinear_a8_workspace_bytes(INT4, 16, 256, 256, 32, ctypes.byref(need)) == QL_E_UNSUPPORTED
+    assert L.qlinear_a8_num_tiles() >= 1
+    r, c = ctypes.c_int(), ctypes.c_int()
+    assert L.qlinear_a8_tile_shape(L.qlinear_a8_num_tiles(), ctypes.byref(r), ctypes.byref(c)) == QL_E_ARG
+
+    def f(M=64, N=256, K=256, fmt=INT4, G=128, x=FAKE, ws=FAKE, wsb=1 << 20, tile=-1, out=FAKE, od=0):
+        return L.qlinear_forward_a8(x, M, N, K, FAKE, FAKE, fmt, G, None, out, od, ws, wsb, tile, None)
+
+    assert f(M=0) == QL_OK
+    assert f(fmt=CB4, G=0) == QL_E_UNSUPPORTED and f(G=32) == QL_E_UNSUPPORTED
+    assert f(tile=99) == QL_E_ARG and f(tile=-2) == QL_E_ARG and f(od=5) == QL_E_ARG
+    assert f(x=None) == QL_E_ARG and f(out=None) == QL_E_ARG
+    assert f(ws=None) == QL_E_WORKSPACE and f(wsb=100) == QL_E_WORKSPACE
+    assert f(x=FAKE + 8) == QL_E_ALIGN and f(ws=FAKE + 16) == QL_E_ALIGN
+    assert L.qlinear_quantize_activations(FAKE, 4, 100, FAKE, FAKE, None) == QL_E_SHAPE
+    assert L.qlinear_quantize_activations(FAKE + 2, 4, 128, FAKE, FAKE, None) == QL_E_ALIGN
+    assert L.qlinear_quantize_activations(FAKE, 0, 128, None, None, None) == QL_OK
