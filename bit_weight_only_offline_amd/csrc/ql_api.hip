@@ -188,7 +188,7 @@ ql_status qlinear_forward_a8(const void *x, int64_t M, int64_t N, int64_t K, con
     if (!aligned(workspace, 256)) return QL_E_ALIGN;
     int8_t *xq = static_cast<int8_t *>(workspace);
     float *xs = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + round256(size_t(M) * size_t(L.Kp)));
-    return from_hip(launch_gemm_a8(L, tile < 0 ? default_a8_tile(M) : tile, static_cast<const uint16_t *>(x), int(M),
+    return from_hip(launch_gemm_a8(L, tile < 0 ? default_a8_tile(M, N, PLAN_CUS) : tile, static_cast<const uint16_t *>(x), int(M),
                                    packed_w, packed_s, bias, out, out_dtype == QL_F32, xq, xs, (hipStream_t)stream));
 }
 

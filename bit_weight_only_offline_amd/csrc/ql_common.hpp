@@ -84,7 +84,14 @@ constexpr int NUM_A8_TILES = 5;
 constexpr A8Tile A8_TILES[NUM_A8_TILES] = {
     {8, 3, 1, 4}, {4, 4, 2, 2}, {4, 4, 1, 4}, {2, 4, 1, 4}, {1, 4, 1, 4},
 };
-inline int default_a8_tile(int64_t M) { return M <= 16 ? 4 : (M <= 32 ? 3 : (M <= 64 ? 2 : 0)); }
+// the largest tile that still gives every compute unit a workgroup, else the smallest
+inline int default_a8_tile(int64_t M, int64_t N, int num_cu) {
+    for (int t = 0; t < NUM_A8_TILES; ++t) {
+        const A8Tile &c = A8_TILES[t];
+        if (ceil_div(M, 16 * c.MT * c.WM) * ceil_div(N, 16 * c.NT * c.WN) >= num_cu) return t;
+    }
+    return NUM_A8_TILES - 1;
+}
 
 // Launch arguments of the linear kernels.
 struct GemmArgs {
