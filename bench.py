@@ -327,7 +327,7 @@ def main():
         print(f"traffic_bytes_per_launch: {traffic}")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        print("bench.py: the library runs on one GPU (it has no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.probe:
         probe(args.probe)
