@@ -131,13 +131,14 @@ struct GemmArgs {
 //           buffer->LDS loads (ql_gemm_lds.hpp); split-K as for kind 1.
 // PF = weight chunks in flight per wavefront (kinds 0, 1) or ring depth (kind 2).
 struct TileCfg { int kind, MT, NT, SK, PF, WK, WM, WN; };
-constexpr int NUM_TILE_CFGS = 19;
+constexpr int NUM_TILE_CFGS = 21;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {0, 1, 1, 0, 4, 8, 1, 1}, {0, 1, 2, 0, 4, 8, 1, 1}, {0, 1, 4, 0, 4, 4, 1, 1}, {0, 1, 1, 0, 8, 4, 1, 1},
     {1, 2, 2, 512, 4, 4, 1, 4}, {1, 4, 2, 256, 4, 4, 1, 4}, {1, 8, 2, 128, 2, 4, 1, 4}, {1, 8, 1, 128, 4, 4, 1, 4},
     {2, 8, 3, 0, 3, 1, 1, 4}, {2, 8, 4, 0, 3, 1, 1, 4}, {2, 4, 4, 0, 3, 1, 2, 2}, {2, 4, 3, 0, 4, 1, 1, 4},
     {2, 2, 4, 0, 4, 1, 1, 4}, {2, 8, 3, 0, 3, 2, 1, 4}, {2, 8, 4, 0, 3, 2, 1, 4}, {2, 4, 4, 0, 4, 2, 1, 4},
     {2, 4, 3, 0, 4, 2, 1, 4}, {2, 2, 4, 0, 6, 1, 1, 4}, {2, 4, 3, 0, 5, 1, 1, 4},
+    {0, 1, 3, 0, 4, 4, 1, 1}, {0, 1, 7, 0, 3, 4, 1, 1},
 };
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.
@@ -214,12 +215,26 @@ inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 //   M <= 256     64-row ring tiles, two wavefronts per tile (INT8: 256 columns);
 //   larger M     128 x 192 ring tiles, two wavefronts per tile (INT formats, whose
 //                group accumulators need the registers: one wavefront per tile).
-inline int default_cfg(const Layout &L, int64_t M) {
-    if (M <= 16) {
-        if (L.ntiles >= 1024) return 2;       // wide: four column tiles per wavefront
-        if (L.ntiles >= 512) return 1;
-        return 0;
+// Decode schedule: the one whose busiest compute unit streams the fewest column tiles,
+// counting one resident workgroup per CU (256 CUs), ties to the wider schedule (fewer
+// rounds of workgroups).  Candidates in order of columns per workgroup: 1, 2, 3, 4, 7.
+inline int decode_cfg(int64_t ntiles) {
+    constexpr int cands[] = {0, 1, 19, 2, 20};
+    int best = 0;
+    int64_t best_load = -1;
+    for (int c : cands) {
+        const int nt = TILE_CFGS[c].NT;
+        const int64_t load = ceil_div(ceil_div(ntiles, nt), 256) * nt;
+        if (best_load < 0 || load <= best_load) {
+            best = c;
+            best_load = load;
+        }
     }
+    return best;
+}
+
+inline int default_cfg(const Layout &L, int64_t M) {
+    if (M <= 16) return decode_cfg(L.ntiles);
     if (M <= 64) return 12;
     const bool intf = L.fmt == FMT_INT4 || L.fmt == FMT_INT8;
     if (M <= 256) return L.fmt == FMT_INT8 ? 15 : 16;
