@@ -57,33 +57,67 @@ hipError_t launch_swiglu(const uint16_t *x, uint16_t *h, int M, int K, hipStream
     return hipGetLastError();
 }
 
-// Grouped launch plan: expert offsets (exclusive prefix sum of the token counts, each
-// count clamped to [0, tokens left] so rows never run past T) and the slot map, expert
-// by expert in order, unused slots marked -1.  One thread: E and the slot count are small
-// and the order is then fixed.
-__global__ void moe_plan_kernel(const int32_t *__restrict__ counts, int E, int T, int rows, int slots,
-                                int *__restrict__ offsets, int *__restrict__ tile_map) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    int run = 0, t = 0;
-    for (int e = 0; e < E; ++e) {
-        const int c = min(max(counts[e], 0), T - run);
-        offsets[e] = run;
-        for (int r = 0; r < c && t < slots; r += rows, ++t) {
-            tile_map[2 * t] = e;
-            tile_map[2 * t + 1] = r;
+// Mixture-of-experts plan: expert offsets (the running sum of the counts, each count
+// clamped to [0, tokens left] so rows never run past T) and the slot map, expert by
+// expert in order, unused slots marked -1.  One workgroup: block-wide prefix sums of the
+// clamped counts and of each expert's number of row blocks, 256 experts at a time; each
+// expert's thread writes its own slots.  The result is the same as walking the experts
+// one by one.
+__global__ void __launch_bounds__(256) moe_plan_kernel(const int32_t *__restrict__ counts, int E, int T, int rows,
+                                                       int slots, int *__restrict__ offsets,
+                                                       int *__restrict__ tile_map) {
+    __shared__ int64_t tok[256];
+    __shared__ int blk[256];
+    const int t = threadIdx.x;
+    int64_t run = 0;                 // clamped tokens of the experts before this batch
+    int used = 0;                    // slots taken by them
+    for (int e0 = 0; e0 < E; e0 += 256) {
+        const int e = e0 + t;
+        const int own = e < E ? min(max(counts[e], 0), T) : 0;
+        tok[t] = own;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {               // inclusive scan of the counts
+            const int64_t v = t >= d ? tok[t - d] : 0;
+            __syncthreads();
+            tok[t] += v;
+            __syncthreads();
         }
-        run += c;
+        const int64_t incl = tok[t], batch = tok[255];
+        const int start = int(min(run + incl - own, int64_t(T)));
+        const int end = int(min(run + incl, int64_t(T)));
+        const int c = end - start;
+        const int nb = (c + rows - 1) / rows;
+        __syncthreads();
+        blk[t] = nb;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {               // inclusive scan of the row blocks
+            const int v = t >= d ? blk[t - d] : 0;
+            __syncthreads();
+            blk[t] += v;
+            __syncthreads();
+        }
+        const int first = used + blk[t] - nb;
+        if (e < E) {
+            offsets[e] = start;
+            for (int r = 0; r < nb && first + r < slots; ++r) {
+                tile_map[2 * (first + r)] = e;
+                tile_map[2 * (first + r) + 1] = r * rows;
+            }
+        }
+        used += blk[255];
+        run = min(run + batch, int64_t(T));
+        __syncthreads();                                  // before the next batch reuses LDS
     }
-    offsets[E] = run;
-    for (; t < slots; ++t) {
-        tile_map[2 * t] = -1;
-        tile_map[2 * t + 1] = 0;
+    if (t == 0) offsets[E] = int(run);
+    for (int k = min(used, slots) + t; k < slots; k += 256) {
+        tile_map[2 * k] = -1;
+        tile_map[2 * k + 1] = 0;
     }
 }
 
 hipError_t launch_moe_plan(const int32_t *counts, int E, int T, int rows, int slots, int *offsets, int *tile_map,
                            hipStream_t st) {
-    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(64), 0, st, counts, E, T, rows, slots, offsets, tile_map);
+    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, counts, E, T, rows, slots, offsets, tile_map);
     return hipGetLastError();
 }
 

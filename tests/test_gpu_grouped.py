@@ -130,3 +130,25 @@ def test_grouped_moe_down_projection_sampled():
     err = np.max(np.concatenate(errs)) / np.sqrt(np.mean(ref ** 2))
     print(f"  sampled {ref.size} outputs: max|dY|/rms = {err:.3e}", flush=True)
     assert err <= TOL
+
+
+def test_grouped_many_experts():
+    """More experts than the plan kernel takes in one batch (300 > 256), most of them
+    empty or with a few tokens, and counts that run past T."""
+    import bit_weight_only_offline_amd as Q
+    fmt, G, N, K, E, T = "mxfp4", 32, 32, 128, 300, 180
+    rng = np.random.default_rng(30)
+    counts = np.where(rng.random(E) < 0.6, 0, rng.integers(1, 4, E)).astype(int)
+    counts[-1] = 50                                        # the running sum passes T here
+    pe, canons, _ = _experts(fmt, G, True, E, N, K, seed=31)
+    x = S.to_bf16_values(rng.standard_normal((T, K)).astype(np.float32))
+    xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    out = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+    Q.grouped_linear(xt, pe, torch.tensor(counts, dtype=torch.int32, device="cuda"), out_dtype=torch.float32,
+                     out=out)
+    torch.cuda.synchronize()
+    yref = O.forward_grouped(fmt, x, canons, list(counts), K, N)
+    y = out.cpu().numpy()
+    done = np.isfinite(yref[:, 0])
+    assert np.array_equal(np.isnan(y[:, 0]), ~done)
+    assert rel_err(y[done], yref[done]) <= TOL
