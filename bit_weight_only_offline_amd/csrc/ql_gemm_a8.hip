@@ -311,6 +311,29 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_a8_kernel(A8Args a) {
     }
 
     // ---- epilogue: row scale, bias, output rounding ----
+    if (m0 + MP <= a.M && (nt0 + NTT) * TILE_N <= a.N) {
+        // a tile wholly inside the output: wave-uniform row pointers, 32-bit lane offsets
+        float bj[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+            bj[j] = a.bias ? bf16_bits_to_f32(a.bias[(nt0 + wn * NTW + j) * TILE_N + c]) : 0.0f;
+        const uint32_t lane_off = uint32_t(g * 4) * uint32_t(a.N) + uint32_t((nt0 + wn * NTW) * TILE_N + c);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + (wm * MTW + mt) * 16 + r;
+                const float rs = a.xs[row + g * 4];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    float v = acc[mt][j][r] * rs;
+                    if (a.bias) v += bj[j];
+                    if (a.out_f32) (reinterpret_cast<float *>(a.out) + row * a.N)[lane_off + j * TILE_N] = v;
+                    else (reinterpret_cast<__bf16 *>(a.out) + row * a.N)[lane_off + j * TILE_N] = (__bf16)v;
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll

@@ -363,6 +363,30 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 rs[j] = reinterpret_cast<const float *>(a.s)[n] * reinterpret_cast<const CbRecord *>(a.aux)->inv_alpha;
         }
     }
+    // a tile wholly inside the output, without a split: no per-element checks, and each
+    // store is a wave-uniform row pointer plus this lane's 32-bit offset
+    if (a.ks == 1 && m0 + MP <= a.M && (nt0 + NTT) * TILE_N <= a.N) {
+        float bj[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+            bj[j] = a.bias ? bf16_bits_to_f32(a.bias[(nt0 + wn * NTW + j) * TILE_N + c]) : 0.0f;
+        const uint32_t lane_off = uint32_t(g * 4) * uint32_t(a.N) + uint32_t((nt0 + wn * NTW) * TILE_N + c);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + (wm * MTW + mt) * 16 + r;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    float v = acc[mt][j][r];
+                    if (FMT == FMT_CB4) v *= rs[j];
+                    if (a.bias) v += bj[j];
+                    if (a.out_f32) (reinterpret_cast<float *>(a.out) + row * a.N)[lane_off + j * TILE_N] = v;
+                    else (reinterpret_cast<__bf16 *>(a.out) + row * a.N)[lane_off + j * TILE_N] = (__bf16)v;
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
