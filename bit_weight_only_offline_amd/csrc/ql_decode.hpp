@@ -31,6 +31,16 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t by
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, BUF_DWORD3);
 }
 
+// A descriptor from values the caller knows to be wave-uniform but the compiler may not
+// (e.g. derived from loads): taken from the first active lane, so it lives in scalar
+// registers and buffer instructions need no per-lane loop.
+__device__ inline __amdgpu_buffer_rsrc_t make_uniform_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t u = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(u))));
+    const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(u >> 32))));
+    return make_rsrc(reinterpret_cast<const void *>((hi << 32) | lo), uint32_t(__builtin_amdgcn_readfirstlane(int(bytes))));
+}
+
 // Ranged loads: a byte offset at or beyond the descriptor's size reads as zero.
 __device__ inline u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);

@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "ql_common.hpp"
 #include "ql_decode.hpp"
@@ -311,27 +312,49 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_a8_kernel(A8Args a) {
     }
 
     // ---- epilogue: row scale, bias, output rounding ----
-    if (m0 + MP <= a.M && (nt0 + NTT) * TILE_N <= a.N) {
-        // a tile wholly inside the output: wave-uniform row pointers, 32-bit lane offsets
+    const int es = a.out_f32 ? 4 : 2;
+    if (m0 + MP <= a.M && (nt0 + NTT) * TILE_N <= a.N &&
+        uint64_t(MP) * uint64_t(a.N) * uint64_t(es) < (uint64_t(1) << 32)) {
+        // a tile wholly inside the output: one ranged buffer for its rows, each store = lane
+        // offset + wave-uniform row offset + column-tile immediate; type and bias chosen once
         float bj[NTW];
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
             bj[j] = a.bias ? bf16_bits_to_f32(a.bias[(nt0 + wn * NTW + j) * TILE_N + c]) : 0.0f;
-        const uint32_t lane_off = uint32_t(g * 4) * uint32_t(a.N) + uint32_t((nt0 + wn * NTW) * TILE_N + c);
+        auto emit = [&](auto f32c, auto biasc) {
+            constexpr bool F32 = decltype(f32c)::value, BIAS = decltype(biasc)::value;
+            constexpr uint32_t ES = F32 ? 4u : 2u;
+            const __amdgpu_buffer_rsrc_t orc = make_uniform_rsrc(static_cast<uint8_t *>(a.out) + int64_t(m0) * a.N * ES,
+                                                                 uint32_t(MP) * uint32_t(a.N) * ES);
+            const uint32_t lane_off =
+                (uint32_t(g * 4) * uint32_t(a.N) + uint32_t((nt0 + wn * NTW) * TILE_N + c)) * ES;
 #pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
+            for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + (wm * MTW + mt) * 16 + r;
-                const float rs = a.xs[row + g * 4];
+                for (int r = 0; r < 4; ++r) {
+                    const int rl = (wm * MTW + mt) * 16 + r;             // row within the tile, lane row g*4 on top
+                    const uint32_t row_off = uint32_t(rl) * uint32_t(a.N) * ES;
+                    const float rsc = a.xs[m0 + rl + g * 4];
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    float v = acc[mt][j][r] * rs;
-                    if (a.bias) v += bj[j];
-                    if (a.out_f32) (reinterpret_cast<float *>(a.out) + row * a.N)[lane_off + j * TILE_N] = v;
-                    else (reinterpret_cast<__bf16 *>(a.out) + row * a.N)[lane_off + j * TILE_N] = (__bf16)v;
+                    for (int j = 0; j < NTW; ++j) {
+                        // the same expression as the checked path below
+                        const float v = BIAS ? fmaf(acc[mt][j][r], rsc, bj[j]) : acc[mt][j][r] * rsc;
+                        if (F32)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orc, int(lane_off + j * TILE_N * ES),
+                                                                  int(row_off), 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), orc,
+                                                                  int(lane_off + j * TILE_N * ES), int(row_off), 0);
+                    }
                 }
-            }
+        };
+        if (a.out_f32) {
+            if (a.bias) emit(std::true_type{}, std::true_type{});
+            else emit(std::true_type{}, std::false_type{});
+        } else {
+            if (a.bias) emit(std::false_type{}, std::true_type{});
+            else emit(std::false_type{}, std::false_type{});
+        }
         return;
     }
 #pragma unroll
@@ -345,8 +368,8 @@ __global__ void __launch_bounds__(64 * WM * WN) qgemm_a8_kernel(A8Args a) {
             for (int j = 0; j < NTW; ++j) {
                 const int n = (nt0 + wn * NTW + j) * TILE_N + c;
                 if (n >= a.N) continue;
-                float v = acc[mt][j][r] * rs;
-                if (a.bias) v += bf16_bits_to_f32(a.bias[n]);
+                // row scale and bias: one fused multiply-add when there is a bias
+                const float v = a.bias ? fmaf(acc[mt][j][r], rs, bf16_bits_to_f32(a.bias[n])) : acc[mt][j][r] * rs;
                 if (a.out_f32) reinterpret_cast<float *>(a.out)[int64_t(m) * a.N + n] = v;
                 else reinterpret_cast<__bf16 *>(a.out)[int64_t(m) * a.N + n] = (__bf16)v;
             }

@@ -26,6 +26,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ql_common.hpp"
 #include "ql_decode.hpp"
 
@@ -363,28 +365,49 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 rs[j] = reinterpret_cast<const float *>(a.s)[n] * reinterpret_cast<const CbRecord *>(a.aux)->inv_alpha;
         }
     }
-    // a tile wholly inside the output, without a split: no per-element checks, and each
-    // store is a wave-uniform row pointer plus this lane's 32-bit offset
-    if (a.ks == 1 && m0 + MP <= a.M && (nt0 + NTT) * TILE_N <= a.N) {
+    // a tile wholly inside the output, without a split: no per-element checks; the tile's
+    // rows are one ranged buffer, each store = this lane's offset + a wave-uniform row
+    // offset + a column-tile immediate, with the output type and the bias chosen once
+    const int es = a.out_f32 ? 4 : 2;
+    if (a.ks == 1 && m0 + MP <= a.M && (nt0 + NTT) * TILE_N <= a.N &&
+        uint64_t(MP) * uint64_t(a.N) * uint64_t(es) < (uint64_t(1) << 32)) {
         float bj[NTW];
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
             bj[j] = a.bias ? bf16_bits_to_f32(a.bias[(nt0 + wn * NTW + j) * TILE_N + c]) : 0.0f;
-        const uint32_t lane_off = uint32_t(g * 4) * uint32_t(a.N) + uint32_t((nt0 + wn * NTW) * TILE_N + c);
+        auto emit = [&](auto f32c, auto biasc) {
+            constexpr bool F32 = decltype(f32c)::value, BIAS = decltype(biasc)::value;
+            constexpr uint32_t ES = F32 ? 4u : 2u;
+            const __amdgpu_buffer_rsrc_t orc = make_uniform_rsrc(static_cast<uint8_t *>(a.out) + int64_t(m0) * a.N * ES,
+                                                                 uint32_t(MP) * uint32_t(a.N) * ES);
+            const uint32_t lane_off =
+                (uint32_t(g * 4) * uint32_t(a.N) + uint32_t((nt0 + wn * NTW) * TILE_N + c)) * ES;
 #pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
+            for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + (wm * MTW + mt) * 16 + r;
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t row_off = uint32_t((wm * MTW + mt) * 16 + r) * uint32_t(a.N) * ES;
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    float v = acc[mt][j][r];
-                    if (FMT == FMT_CB4) v *= rs[j];
-                    if (a.bias) v += bj[j];
-                    if (a.out_f32) (reinterpret_cast<float *>(a.out) + row * a.N)[lane_off + j * TILE_N] = v;
-                    else (reinterpret_cast<__bf16 *>(a.out) + row * a.N)[lane_off + j * TILE_N] = (__bf16)v;
+                    for (int j = 0; j < NTW; ++j) {
+                        // the same expression as the checked path below
+                        const float v = FMT == FMT_CB4 ? (BIAS ? fmaf(acc[mt][j][r], rs[j], bj[j]) : acc[mt][j][r] * rs[j])
+                                                       : (BIAS ? acc[mt][j][r] + bj[j] : acc[mt][j][r]);
+                        if (F32)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orc, int(lane_off + j * TILE_N * ES),
+                                                                  int(row_off), 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), orc,
+                                                                  int(lane_off + j * TILE_N * ES), int(row_off), 0);
+                    }
                 }
-            }
+        };
+        if (a.out_f32) {
+            if (a.bias) emit(std::true_type{}, std::true_type{});
+            else emit(std::true_type{}, std::false_type{});
+        } else {
+            if (a.bias) emit(std::false_type{}, std::true_type{});
+            else emit(std::false_type{}, std::false_type{});
+        }
         return;
     }
 #pragma unroll
@@ -398,9 +421,10 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 if (m >= a.M) continue;
                 if (a.ks == 1) {
                     if (n >= a.N) continue;
-                    float v = acc[mt][j][r];
-                    if (FMT == FMT_CB4) v *= rs[j];
-                    if (a.bias) v += bf16_bits_to_f32(a.bias[n]);
+                    // codebook row scale and bias: one fused multiply-add when both apply
+                    const float b = a.bias ? bf16_bits_to_f32(a.bias[n]) : 0.0f;
+                    const float v = FMT == FMT_CB4 ? (a.bias ? fmaf(acc[mt][j][r], rs[j], b) : acc[mt][j][r] * rs[j])
+                                                   : (a.bias ? acc[mt][j][r] + b : acc[mt][j][r]);
                     if (a.out_f32) reinterpret_cast<float *>(a.out)[int64_t(m) * a.N + n] = v;
                     else reinterpret_cast<__bf16 *>(a.out)[int64_t(m) * a.N + n] = (__bf16)v;
                 } else if (n < a.Np) {
