@@ -186,18 +186,22 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
         return (GS <= STEPS) ? uint32_t(kc * (STEPS / GS) + q) : uint32_t(kc / (GS / STEPS));
     };
 
+    // only the last chunk can reach past K: this lane's pieces of it that do are marked
+    // out of range once, here, and the mark is applied to that chunk alone
+    uint32_t tail_mask[NA / W];
+#pragma unroll
+    for (int q = 0; q < NA / W; ++q)
+        tail_mask[q] = ((a.kchunks - 1) * CH + a_k[q] >= a.K) ? 0x80000000u : 0u;
+
     // issue the loads of chunk i (relative) into ring buffer buf
     auto issue = [&](int i, int buf) {
         const int kc = chunk_of(i);
         uint8_t *base = lds + buf * STAGE;
-        const int kbase = kc * CH;
-        const bool whole = kbase + CH <= a.K;               // wave-uniform: no input past K
+        const uint32_t kbase2 = uint32_t(kc * CH) * 2u;
+        const uint32_t last = kc == a.kchunks - 1 ? 0xFFFFFFFFu : 0u;      // wave-uniform
 #pragma unroll
-        for (int q = 0; q < NA / W; ++q) {
-            uint32_t off = a_off[q] + uint32_t(kbase) * 2u;
-            if (!whole && kbase + a_k[q] >= a.K) off |= 0x80000000u;
-            ld128_lds(xr, off, base + (wv + W * q) * 1024);
-        }
+        for (int q = 0; q < NA / W; ++q)
+            ld128_lds(xr, ((tail_mask[q] & last) | a_off[q]) + kbase2, base + (wv + W * q) * 1024);
 #pragma unroll
         for (int q = 0; q < NBW; ++q)
             ld128_lds(wr, b_off[q] + uint32_t(kc) * TILE_BYTES, base + A_BYTES + ((wv + W * q) % NB) * 1024);
