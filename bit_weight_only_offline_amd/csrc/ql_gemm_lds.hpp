@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kh = wv / (WM * WN);                  // which k-steps of each chunk
+    const int kh = WKK == 1 ? 0 : wv / (WM * WN);  // which k-steps of each chunk
     const int wm = (wv % (WM * WN)) / WN, wn = wv % WN;
     // B tiles are dealt round-robin, every wavefront issuing NBW loads: tile (wv + W q) mod
     // NB, so when W does not divide NB a few tiles are fetched twice (identical bytes to
@@ -227,16 +227,35 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     const u32x4 ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const bf16x8 ones = as_bf16x8(ones_u);
 
+    // this lane's A-fragment addresses inside a stage, for each of its k-steps of a chunk
+    uint32_t a_frag[SPW][MTW];
+#pragma unroll
+    for (int tt = 0; tt < SPW; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+            a_frag[tt][mt] = uint32_t(XBlock<FMT>::slot((wm * MTW + mt) * 16 + c, 4 * (kh * SPW + tt) + g));
+    // this wavefront's words of a lane's 16-byte weight record: all four, or with two
+    // k-halves the two of its half (4-bit formats: one word per k-step; INT8: two)
+    constexpr int WPW = 4 / WKK;
+    static_assert(WKK == 1 || WKK == 2, "one or two k-halves");
+
     auto compute = [&](int i, int buf) {
         const int kc = chunk_of(i);
         const uint8_t *A = lds + buf * STAGE;
         const uint8_t *Bt = A + A_BYTES;
         const uint8_t *sc = A + A_BYTES + B_BYTES + wv * SCW;
-        u32x4 wq[NTW];
+        uint32_t wq[NTW][WPW];
         uint32_t sq[NTW][SPC], zq[NTW][SPC];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-            wq[j] = *reinterpret_cast<const u32x4 *>(Bt + (wn * NTW + j) * 1024 + lane * 16);
+            const uint8_t *rec = Bt + (wn * NTW + j) * 1024 + lane * 16;
+            if constexpr (WKK == 1) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(rec);
+                wq[j][0] = v.x; wq[j][1] = v.y; wq[j][2] = v.z; wq[j][3] = v.w;
+            } else {
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(rec + kh * 8);
+                wq[j][0] = v.x; wq[j][1] = v.y;
+            }
 #pragma unroll
             for (int q = 0; q < SPC; ++q) {
                 if (FMT == FMT_MXFP4) {
@@ -252,15 +271,14 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
             const int t = kh * SPW + tt;
             bf16x8 af[MTW];
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt)
-                af[mt] = *reinterpret_cast<const bf16x8 *>(A + XBlock<FMT>::slot((wm * MTW + mt) * 16 + c, 4 * t + g));
+            for (int mt = 0; mt < MTW; ++mt) af[mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt][mt]);
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 u32x4 bw;
-                if (FMT == FMT_INT4) bw = dec_int4(wq[j][t]);
-                else if (FMT == FMT_INT8) bw = dec_int8(wq[j][2 * t], wq[j][2 * t + 1]);
-                else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][t], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
-                else bw = dec_cb4(wq[j][t], lut);
+                if (FMT == FMT_INT4) bw = dec_int4(wq[j][tt]);
+                else if (FMT == FMT_INT8) bw = dec_int8(wq[j][2 * tt], wq[j][2 * tt + 1]);
+                else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][tt], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
+                else bw = dec_cb4(wq[j][tt], lut);
                 const bf16x8 bv = as_bf16x8(bw);
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt) {
