@@ -188,7 +188,8 @@ __global__ void __launch_bounds__(WG_THREADS) qmm_kernel(GemmArgs a) {
             }
             if (INTF) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) xs[mt] = mfma16x16x32(af[mt], ones, xs[mt]);
+                for (int mt = 0; mt < MT; ++mt)
+                    if (FMT == FMT_INT4) xs[mt] = mfma16x16x32(af[mt], ones, xs[mt]);   // INT8 codes are signed
                 bool boundary;
                 if (GS <= STEPS) boundary = ((t + 1) % GS) == 0;
                 else boundary = (t == STEPS - 1) && (((kc + 1) % (GS / STEPS)) == 0);
@@ -203,7 +204,7 @@ __global__ void __launch_bounds__(WG_THREADS) qmm_kernel(GemmArgs a) {
                             off = ZP ? 128.0f + float((zq[j][q] >> z_shift) & 0xFu) : 136.0f;
                         } else {
                             s = bf16_bits_to_f32(sbits);
-                            off = 128.0f;
+                            off = 0.0f;                   // the operand is the signed code
                         }
                         const float cz = -s * off;
 #pragma unroll
@@ -211,7 +212,7 @@ __global__ void __launch_bounds__(WG_THREADS) qmm_kernel(GemmArgs a) {
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 acc[mt][j][r] = fmaf(s, tmp[mt][j][r], acc[mt][j][r]);
-                                acc[mt][j][r] = fmaf(cz, xs[mt][r], acc[mt][j][r]);
+                                if (FMT == FMT_INT4) acc[mt][j][r] = fmaf(cz, xs[mt][r], acc[mt][j][r]);
                             }
                             tmp[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                         }

@@ -288,7 +288,8 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
             }
             if (INTF) {
 #pragma unroll
-                for (int mt = 0; mt < MTW; ++mt) xs[mt] = mfma16x16x32(af[mt], ones, xs[mt]);
+                for (int mt = 0; mt < MTW; ++mt)
+                    if (FMT == FMT_INT4) xs[mt] = mfma16x16x32(af[mt], ones, xs[mt]);   // INT8 codes are signed
                 // fold the partial group sums at the last of this wavefront's steps in
                 // the group (a group may span both halves of a chunk, or several chunks)
                 bool boundary;
@@ -305,7 +306,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                             off = ZP ? 128.0f + float((zq[j][q] >> z_shift) & 0xFu) : 136.0f;
                         } else {
                             s = bf16_bits_to_f32(sbits);
-                            off = 128.0f;
+                            off = 0.0f;                   // the operand is the signed code
                         }
                         const float cz = -s * off;
 #pragma unroll
@@ -313,7 +314,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 acc[mt][j][r] = fmaf(s, tmp[mt][j][r], acc[mt][j][r]);
-                                acc[mt][j][r] = fmaf(cz, xs[mt][r], acc[mt][j][r]);
+                                if (FMT == FMT_INT4) acc[mt][j][r] = fmaf(cz, xs[mt][r], acc[mt][j][r]);
                             }
                             tmp[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                         }

@@ -207,7 +207,7 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                 else acc[j] = mfma16x16x32(af, as_bf16x8(bw), acc[j]);
             }
             if (INTF) {
-                xs = mfma16x16x32(af, ones, xs);
+                if (FMT == FMT_INT4) xs = mfma16x16x32(af, ones, xs);   // INT8 codes are signed
                 bool boundary;
                 if (GS <= STEPS) boundary = ((t + 1) % GS) == 0;
                 else boundary = (t == STEPS - 1) && (((kc + 1) % (GS / STEPS)) == 0);
@@ -222,13 +222,13 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                             off = ZP ? 128.0f + float((zq[j][q] >> z_shift) & 0xFu) : 136.0f;
                         } else {
                             s = bf16_bits_to_f32(sbits);
-                            off = 128.0f;
+                            off = 0.0f;                   // the operand is the signed code
                         }
                         const float cz = -s * off;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             acc[j][r] = fmaf(s, tmp[j][r], acc[j][r]);
-                            acc[j][r] = fmaf(cz, xs[r], acc[j][r]);
+                            if (FMT == FMT_INT4) acc[j][r] = fmaf(cz, xs[r], acc[j][r]);
                         }
                         tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }

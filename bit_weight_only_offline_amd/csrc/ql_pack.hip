@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(256) dequant_tile_kernel(const u32x4 *__restri
         scale = (FMT == FMT_INT4) ? f16_bits_to_f32(sb) : bf16_bits_to_f32(sb);
         float off;
         if (FMT == FMT_INT8) {
-            off = 128.0f;
+            off = 0.0f;                          // the INT8 operand is the signed code
         } else if (zeros) {
             const uint8_t zb = z[(int64_t(nt) * ngroups + grp) * 8 + (c >> 1)];
             off = 128.0f + float((zb >> (4 * (c & 1))) & 0xF);

@@ -113,7 +113,7 @@ def test_dequant_tile_bit_exact(case):
 
 def test_dequant_tile_operand_mode_is_exact_bf16_image():
     """Mode 1: the matrix-core operand is an exact bf16 image of the code (INT4: 128+u,
-    INT8: q+128, MXFP4: the scaled value, CB4: +-bf16(alpha*c[8+m]))."""
+    INT8: the signed code q, MXFP4: the scaled value, CB4: +-bf16(alpha*c[8+m]))."""
     Q = _lib()
     case = ("int4_asym_g128", "int4", 128, False, 32, 256)
     pw, canon, _ = _packed(case)
@@ -123,7 +123,7 @@ def test_dequant_tile_operand_mode_is_exact_bf16_image():
     case = ("int8_g256", "int8", 256, True, 32, 256)
     pw, canon, _ = _packed(case)
     op = Q.dequant_tile(pw, mode=1).cpu().numpy()
-    assert np.array_equal(op, canon["codes"].astype(np.float32) + 128.0)
+    assert np.array_equal(op, canon["codes"].astype(np.float32))
     case = ("cb4", "cb4", 0, True, 32, 256)
     pw, canon, _ = _packed(case)
     op = Q.dequant_tile(pw, mode=1).cpu().numpy()
