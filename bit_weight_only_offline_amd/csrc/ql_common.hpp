@@ -238,7 +238,7 @@ inline int default_cfg(const Layout &L, int64_t M) {
     if (M <= 64) return 12;
     const bool intf = L.fmt == FMT_INT4 || L.fmt == FMT_INT8;
     if (M <= 256) return L.fmt == FMT_INT8 ? 15 : 16;
-    if (L.fmt == FMT_INT8) return 16;
+    if (L.fmt == FMT_INT8) return 13;
     return intf ? 8 : 13;
 }
 
