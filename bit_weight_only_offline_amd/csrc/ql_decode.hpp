@@ -3,7 +3,9 @@
 //
 // The B operand is always an exact bf16 image of the code:
 //   INT4   offset-binary code u in 0..15  ->  bf16(128 + u)       (one AND-OR per pair)
-//   INT8   offset-binary code u in 0..255 ->  bf16(u - 128)       (byte -> f32 -> bf16)
+//   INT8   offset-binary code u in 0..255 ->  bf16(u - 128) in the tile kernels, bf16(u)
+//          in the decode kernel (where one fewer operation per value matters more than
+//          the extra activation-sum MFMA)              (byte -> f32 -> bf16)
 //   MXFP4  E2M1 code with its E8M0 scale  ->  bf16(e2m1 * 2^(e-127))  (hardware convert)
 //   CB4    sign-magnitude index           ->  +-bf16(alpha * c[8 + m])  (byte permutes)
 // INT4's offset (128, plus 8 or its zero-point), group scales and codebook row scales are
@@ -169,14 +171,17 @@ __device__ inline u32x4 dec_int4(uint32_t w) {
     return r;
 }
 
-// ---- INT8: eight offset-binary bytes (two words) -> bf16(u - 128) = bf16(q), exact ------
-// (the signed code itself, so the symmetric INT8 product needs no activation-sum term)
+// ---- INT8: eight offset-binary bytes (two words) -> bf16(u - 128) = bf16(q) (SIGNED: the
+// code itself, no activation-sum term needed) or bf16(u) (one operation fewer per value;
+// the offset 128 is then folded with the activation sum), both exact ----------------------
+template <bool SIGNED>
 __device__ inline u32x4 dec_int8(uint32_t d0, uint32_t d1) {
+    const float o = SIGNED ? 128.0f : 0.0f;
     u32x4 r;
-    r.x = pack_bf16x2((float)(d0 & 0xFFu) - 128.0f, (float)((d0 >> 8) & 0xFFu) - 128.0f);
-    r.y = pack_bf16x2((float)((d0 >> 16) & 0xFFu) - 128.0f, (float)(d0 >> 24) - 128.0f);
-    r.z = pack_bf16x2((float)(d1 & 0xFFu) - 128.0f, (float)((d1 >> 8) & 0xFFu) - 128.0f);
-    r.w = pack_bf16x2((float)((d1 >> 16) & 0xFFu) - 128.0f, (float)(d1 >> 24) - 128.0f);
+    r.x = pack_bf16x2((float)(d0 & 0xFFu) - o, (float)((d0 >> 8) & 0xFFu) - o);
+    r.y = pack_bf16x2((float)((d0 >> 16) & 0xFFu) - o, (float)(d0 >> 24) - o);
+    r.z = pack_bf16x2((float)(d1 & 0xFFu) - o, (float)((d1 >> 8) & 0xFFu) - o);
+    r.w = pack_bf16x2((float)((d1 >> 16) & 0xFFu) - o, (float)(d1 >> 24) - o);
     return r;
 }
 

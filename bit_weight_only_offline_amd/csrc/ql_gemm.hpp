@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(WG_THREADS) qmm_kernel(GemmArgs a) {
             for (int j = 0; j < NT; ++j) {
                 u32x4 bw;
                 if (FMT == FMT_INT4) bw = dec_int4(wq[j][t]);
-                else if (FMT == FMT_INT8) bw = dec_int8(wq[j][2 * t], wq[j][2 * t + 1]);
+                else if (FMT == FMT_INT8) bw = dec_int8<true>(wq[j][2 * t], wq[j][2 * t + 1]);
                 else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][t], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
                 else bw = dec_cb4(wq[j][t], lut);
                 const bf16x8 b = as_bf16x8(bw);

@@ -276,7 +276,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
             for (int j = 0; j < NTW; ++j) {
                 u32x4 bw;
                 if (FMT == FMT_INT4) bw = dec_int4(wq[j][tt]);
-                else if (FMT == FMT_INT8) bw = dec_int8(wq[j][2 * tt], wq[j][2 * tt + 1]);
+                else if (FMT == FMT_INT8) bw = dec_int8<true>(wq[j][2 * tt], wq[j][2 * tt + 1]);
                 else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][tt], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
                 else bw = dec_cb4(wq[j][tt], lut);
                 const bf16x8 bv = as_bf16x8(bw);

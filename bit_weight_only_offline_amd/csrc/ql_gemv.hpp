@@ -200,14 +200,14 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
             for (int j = 0; j < NT; ++j) {
                 u32x4 bw;
                 if (FMT == FMT_INT4) bw = dec_int4(wq[j][t]);
-                else if (FMT == FMT_INT8) bw = dec_int8(wq[j][2 * t], wq[j][2 * t + 1]);
+                else if (FMT == FMT_INT8) bw = dec_int8<false>(wq[j][2 * t], wq[j][2 * t + 1]);
                 else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][t], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
                 else bw = dec_cb4(wq[j][t], lut);
                 if (INTF) tmp[j] = mfma16x16x32(af, as_bf16x8(bw), tmp[j]);
                 else acc[j] = mfma16x16x32(af, as_bf16x8(bw), acc[j]);
             }
             if (INTF) {
-                if (FMT == FMT_INT4) xs = mfma16x16x32(af, ones, xs);   // INT8 codes are signed
+                xs = mfma16x16x32(af, ones, xs);
                 bool boundary;
                 if (GS <= STEPS) boundary = ((t + 1) % GS) == 0;
                 else boundary = (t == STEPS - 1) && (((kc + 1) % (GS / STEPS)) == 0);
@@ -222,13 +222,13 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                             off = ZP ? 128.0f + float((zq[j][q] >> z_shift) & 0xFu) : 136.0f;
                         } else {
                             s = bf16_bits_to_f32(sbits);
-                            off = 0.0f;                   // the operand is the signed code
+                            off = 128.0f;                 // the operand here is bf16(u), u = q + 128
                         }
                         const float cz = -s * off;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             acc[j][r] = fmaf(s, tmp[j][r], acc[j][r]);
-                            if (FMT == FMT_INT4) acc[j][r] = fmaf(cz, xs[r], acc[j][r]);
+                            acc[j][r] = fmaf(cz, xs[r], acc[j][r]);
                         }
                         tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }

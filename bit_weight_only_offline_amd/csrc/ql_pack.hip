@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(256) dequant_tile_kernel(const u32x4 *__restri
     if (FMT == FMT_INT4) {
         op = dec_int4(rec[t]);
     } else if (FMT == FMT_INT8) {
-        op = dec_int8(rec[2 * t], rec[2 * t + 1]);
+        op = dec_int8<true>(rec[2 * t], rec[2 * t + 1]);
     } else if (FMT == FMT_MXFP4) {
         const uint32_t sw = reinterpret_cast<const uint32_t *>(s)[(int64_t(nt) * kchunks + kc) * TILE_N + c];
         op = dec_mxfp4(rec[t], e8m0_to_f32((sw >> (8 * t)) & 0xFFu));
