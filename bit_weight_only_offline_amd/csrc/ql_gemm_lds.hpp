@@ -15,8 +15,9 @@
 //      land at l*16, exactly where the lane that decodes them reads).
 // Per stage every wavefront waits for its own loads (s_waitcnt vmcnt), one barrier makes
 // all of them visible and frees the oldest buffer, the loads of the stage S-1 ahead are
-// issued, and the chunk is consumed: one ds_read_b128 per packed tile, register decode,
-// MTW x NTW MFMAs per k-step.  Each wavefront's scale and zero-point words of the chunk
+// issued, and the chunk is consumed: one read per packed tile (the lane's 16-byte record,
+// or with two k-halves the 8 bytes of its half), register decode, MTW x NTW MFMAs per
+// k-step.  Each wavefront's scale and zero-point words of the chunk
 // ride in the same stage (4-byte direct loads), so every load of the loop goes to LDS
 // and every wait is explicit.  Out-of-range
 // rows and inputs load as zero (ranged buffer loads).  Workgroups are numbered so that
