@@ -329,10 +329,17 @@ _WS = {}
 
 
 def workspace(device, nbytes: int) -> torch.Tensor:
-    """A shared workspace of at least nbytes on device, reused across calls (the library
-    does not depend on its contents on entry)."""
+    """A shared workspace of at least nbytes on device, reused across calls on the
+    device's current stream (the library does not depend on its contents on entry).
+
+    There is one per (device, stream): calls on one stream run in order, so they may share
+    it, while calls on two streams may overlap and must not.  It is allocated while that
+    stream is current, so when it grows, the old buffer goes back to torch's allocator
+    ordered after the work already queued on the stream."""
     d = torch.device(device)
-    key = (d.type, d.index if d.index is not None else torch.cuda.current_device())
+    if d.index is None:
+        d = torch.device(d.type, torch.cuda.current_device())
+    key = (d.type, d.index, torch.cuda.current_stream(d).cuda_stream)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=d)
