@@ -47,6 +47,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 POOL_BYTES = 1 << 30           # > 2 x the 256 MB Infinity Cache
+AUX_WARM_S = 0.25              # untimed replays before each timed leg after the main step
 COPY_BYTES = 256 << 20         # calibration copy for the traffic counters
 
 # sources that define the decode kernel the roofline reports on; a recorded traffic
@@ -189,14 +190,18 @@ def summarize_pmc(fetch_dir, write_dir):
     return out, int(round(traffic))
 
 
-def time_forward(Q, pool, x, act, steps, warmup, use_graph=True, schedule=None):
-    """Average time (ms) of one forward over `steps` forwards, each on the next pool copy."""
+def time_forward(Q, pool, x, act, steps, warmup, use_graph=True, schedule=None, warm_s=0.0, reps=1):
+    """Average time (ms) of one forward over `steps` forwards, each on the next pool copy.
+
+    With a graph: one untimed replay, then more untimed replays until warm_s seconds have
+    passed (so the clocks have settled under this load), then `reps` timed replays of the
+    `steps` forwards; the median replay is returned."""
     import torch
     pw0 = pool[0]
     M = x.shape[0]
     out = torch.empty((M, pw0.N), dtype=torch.bfloat16, device=x.device)
     wsb = Q.workspace_bytes(pw0.fmt, M, pw0.N, pw0.K, pw0.group, act, schedule)
-    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=x.device)   # counters start at zero
+    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=x.device)
 
     def run(i):
         Q.linear(x, pool[i % len(pool)], act=act, out=out, workspace=ws, schedule=schedule)
@@ -215,12 +220,19 @@ def time_forward(Q, pool, x, act, steps, warmup, use_graph=True, schedule=None):
         torch.cuda.synchronize()
         g.replay()                     # warm replay
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            g.replay()
+            torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / steps)
+        ms = sorted(times)[len(times) // 2]
         del g
     else:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -364,9 +376,12 @@ def main():
 
     # ---- prefill: 4-bit codebook, 3072 x 3072, M = 2048 ----
     wl5 = S.WORKLOADS["cb4_prefill"]
-    pool5 = _pool(Q, "cb4", wl5["N"], wl5["K"], 0, True, 5, 256 << 20)
+    # every forward reads the next copy of a 1 GiB pool, all copies once per replay, so the
+    # weights come from HBM, not from the Infinity Cache
+    pool5 = _pool(Q, "cb4", wl5["N"], wl5["K"], 0, True, 5, POOL_BYTES)
     x5 = torch.from_numpy(S.activations(wl5, 2048)).cuda().to(torch.bfloat16)
-    ms5, _ = time_forward(Q, pool5, x5, None, max(20, args.steps // 4), max(3, args.warmup // 4), use_graph)
+    ms5, _ = time_forward(Q, pool5, x5, None, max(len(pool5), args.steps // 4), max(3, args.warmup // 4), use_graph,
+                          warm_s=AUX_WARM_S, reps=3)
     fl = 2.0 * 2048 * wl5["N"] * wl5["K"]
     tflops = fl / (ms5 * 1e-3) / 1e12
     prefill = {"workload": "cb4 Lloyd-Max codebook 3072x3072, M=2048, bf16", "us": round(ms5 * 1e3, 2),
@@ -385,7 +400,8 @@ def main():
             for M in M_list:
                 xa = torch.from_numpy(S.activations(w_, M)).cuda().to(torch.bfloat16)
                 act = "swiglu" if w_.get("swiglu") else None
-                ms, _ = time_forward(Q, pl, xa, act, max(20, args.steps // 4), 5, use_graph)
+                ms, _ = time_forward(Q, pl, xa, act, max(20, len(pl), args.steps // 4), 5, use_graph,
+                                     warm_s=AUX_WARM_S, reps=3)
                 b = alg_bytes(fmt, M, w_["N"], w_["K"], w_["group"], False, bool(act), w_.get("bias_std") is not None)
                 fl = 2.0 * M * w_["N"] * w_["K"]
                 others[f"{name}/M{M}"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
@@ -483,16 +499,21 @@ def main():
                 outa = torch.empty(M, 3072, device="cuda", dtype=torch.bfloat16)
                 wsa = torch.empty(Q.a8_workspace_bytes(fmt_, M, 3072, 3072, G_) + 256, dtype=torch.uint8,
                                   device="cuda")
-                for i in range(3):
-                    Q.linear_a8(xa, pl[i % len(pl)], out=outa, workspace=wsa)
-                torch.cuda.synchronize()
+                n_a8 = max(40, len(pl))      # every pool copy once: weights from HBM
+                t0 = time.perf_counter()
+                while True:
+                    for i in range(n_a8):
+                        Q.linear_a8(xa, pl[i % len(pl)], out=outa, workspace=wsa)
+                    torch.cuda.synchronize()
+                    if time.perf_counter() - t0 >= AUX_WARM_S:
+                        break
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                for i in range(40):
+                for i in range(n_a8):
                     Q.linear_a8(xa, pl[i % len(pl)], out=outa, workspace=wsa)
                 e1.record()
                 torch.cuda.synchronize()
-                ms = e0.elapsed_time(e1) / 40
+                ms = e0.elapsed_time(e1) / n_a8
                 a8[f"{fmt_}_g{G_}_3072/M{M}"] = {"us": round(ms * 1e3, 2),
                                                  "TOPS": round(2.0 * M * 3072 * 3072 / (ms * 1e-3) / 1e12, 1)}
             del pl
