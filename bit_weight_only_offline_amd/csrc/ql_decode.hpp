@@ -207,16 +207,18 @@ struct CbLut {
 __device__ inline u32x4 dec_cb4(uint32_t w, const CbLut &L) {
     const uint32_t sa = w & 0x07070707u;          // magnitudes of elements 0,2,1,3
     const uint32_t sb = (w >> 4) & 0x07070707u;   // magnitudes of elements 4,6,5,7
-    const uint32_t ha = __builtin_amdgcn_perm(L.hi1, L.hi0, sa);
+    // high bytes with their signs: the sign of the element in byte i of sa is bit 8i+3
+    // of w, that of byte i of sb is bit 8i+7; both go to bit 7 of that high byte
+    const uint32_t sg = 0x80808080u;
+    const uint32_t ha = __builtin_amdgcn_perm(L.hi1, L.hi0, sa) ^ ((w << 4) & sg);
     const uint32_t la = __builtin_amdgcn_perm(L.lo1, L.lo0, sa);
-    const uint32_t hb = __builtin_amdgcn_perm(L.hi1, L.hi0, sb);
+    const uint32_t hb = __builtin_amdgcn_perm(L.hi1, L.hi0, sb) ^ (w & sg);
     const uint32_t lb = __builtin_amdgcn_perm(L.lo1, L.lo0, sb);
-    const uint32_t sg = 0x80008000u;
     u32x4 r;
-    r.x = __builtin_amdgcn_perm(ha, la, 0x06020400u) ^ ((w << 12) & sg);   // elements 0, 1
-    r.y = __builtin_amdgcn_perm(ha, la, 0x07030501u) ^ ((w << 4) & sg);    // elements 2, 3
-    r.z = __builtin_amdgcn_perm(hb, lb, 0x06020400u) ^ ((w << 8) & sg);    // elements 4, 5
-    r.w = __builtin_amdgcn_perm(hb, lb, 0x07030501u) ^ (w & sg);           // elements 6, 7
+    r.x = __builtin_amdgcn_perm(ha, la, 0x06020400u);   // elements 0, 1
+    r.y = __builtin_amdgcn_perm(ha, la, 0x07030501u);   // elements 2, 3
+    r.z = __builtin_amdgcn_perm(hb, lb, 0x06020400u);   // elements 4, 5
+    r.w = __builtin_amdgcn_perm(hb, lb, 0x07030501u);   // elements 6, 7
     return r;
 }
 

@@ -267,12 +267,26 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 }
             }
         }
+        // A fragments: with the codebook and MXFP4 (no group-sum registers) every k-step's
+        // fragments of the chunk are read up front, so the reads of the later k-steps are
+        // in flight during the MFMAs of the first; otherwise k-step by k-step
+        constexpr int AHOLD = INTF ? 1 : SPW;
+        bf16x8 afs[AHOLD][MTW];
+        if constexpr (AHOLD > 1) {
+#pragma unroll
+            for (int tt = 0; tt < SPW; ++tt)
+#pragma unroll
+                for (int mt = 0; mt < MTW; ++mt) afs[tt][mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt][mt]);
+            __builtin_amdgcn_sched_barrier(0);     // keep the reads ahead of the MFMAs
+        }
 #pragma unroll
         for (int tt = 0; tt < SPW; ++tt) {
             const int t = kh * SPW + tt;
-            bf16x8 af[MTW];
+            bf16x8 *af = afs[AHOLD > 1 ? tt : 0];
+            if constexpr (AHOLD == 1) {
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt) af[mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt][mt]);
+                for (int mt = 0; mt < MTW; ++mt) af[mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt][mt]);
+            }
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 u32x4 bw;
