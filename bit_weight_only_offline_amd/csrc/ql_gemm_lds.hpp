@@ -188,7 +188,10 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     };
 
     // only the last chunk can reach past K: this lane's pieces of it that do are marked
-    // out of range once, here, and the mark is applied to that chunk alone
+    // out of range once, here, and the mark is applied to that chunk alone.  The mark is
+    // ORed into the finished offset: every in-range offset is below 2^31, and a
+    // past-K offset added after the mark could carry out of bit 31 and wrap back into
+    // the buffer when the activations fill nearly 2 GiB
     uint32_t tail_mask[NA / W];
 #pragma unroll
     for (int q = 0; q < NA / W; ++q)
@@ -202,7 +205,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
         const uint32_t last = kc == a.kchunks - 1 ? 0xFFFFFFFFu : 0u;      // wave-uniform
 #pragma unroll
         for (int q = 0; q < NA / W; ++q)
-            ld128_lds(xr, ((tail_mask[q] & last) | a_off[q]) + kbase2, base + (wv + W * q) * 1024);
+            ld128_lds(xr, (a_off[q] + kbase2) | (tail_mask[q] & last), base + (wv + W * q) * 1024);
 #pragma unroll
         for (int q = 0; q < NBW; ++q)
             ld128_lds(wr, b_off[q] + uint32_t(kc) * TILE_BYTES, base + A_BYTES + ((wv + W * q) % NB) * 1024);
