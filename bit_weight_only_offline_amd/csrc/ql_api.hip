@@ -240,6 +240,11 @@ ql_status qlinear_tile_shape(int tile, int *rows, int *cols, int *kblock) {
 
 namespace {
 
+// Launch-grid limits of the device: the x dimension takes up to 2^31 - 1 workgroups, the
+// y and z dimensions 65536 (hipDeviceProp_t::maxGridSize on gfx950); 65535 is used.
+constexpr int64_t GRID_X_MAX = (int64_t(1) << 31) - 1;
+constexpr int64_t GRID_YZ_MAX = 65535;
+
 // Resolve a (possibly partial) schedule into a launch plan.
 ql_status plan_for(ql_format f, int64_t M, int64_t N, int64_t K, int group, int has_zeros, ql_act act,
                    const ql_schedule *sched, Layout *L, Plan *p) {
@@ -254,6 +259,11 @@ ql_status plan_for(ql_format f, int64_t M, int64_t N, int64_t K, int group, int 
     }
     if (is_decode(cfg) && (M > 16 || splits > 1)) return QL_E_UNSUPPORTED;   // decode: M <= 16, no split
     *p = make_plan(*L, M, cfg, splits, PLAN_CUS, act == QL_ACT_SWIGLU);
+    // grid: decode (column blocks); ring tiles (row x column blocks, splits); tiles of
+    // kind 1 (column blocks, row blocks, splits)
+    const int kind = TILE_CFGS[cfg].kind;
+    const int64_t gx = kind == 2 ? int64_t(p->mtiles) * p->nblocks : int64_t(p->nblocks);
+    if (gx > GRID_X_MAX || p->ks > GRID_YZ_MAX || (kind == 1 && p->mtiles > GRID_YZ_MAX)) return QL_E_UNSUPPORTED;
     return QL_OK;
 }
 
@@ -266,13 +276,16 @@ struct GroupedPlan {
     Plan plan;
     int rows = 0;
     size_t ws_bytes = 0;
+    bool fits = true;    // the launch grid is within the device's limits
 };
 GroupedPlan grouped_plan(int64_t T, int64_t E, int64_t N, int64_t K, ql_format f, int group) {
     GroupedPlan g;
     const Layout L = layout_of(f, N, K, group, 0);
     const int64_t per = (T + E - 1) / E;
     int cfg;
-    if (per <= 16) cfg = default_cfg(L, 16);            // decode kernel, slots of 16 rows
+    // (the decode kernel takes the slots as the grid's y dimension: past its limit the
+    // 32-row ring tile, with the slots along x, serves instead)
+    if (per <= 16 && ceil_div(T, 16) + E <= GRID_YZ_MAX) cfg = default_cfg(L, 16);   // decode, 16-row slots
     else if (per <= 48) cfg = 12;                        // 32 x 256
     else if (per <= 96) cfg = 16;                        // 64 x 192, two waves per tile
     else cfg = (f == QL_INT4 || f == QL_INT8) ? 8 : 13;  // 128 x 192
@@ -282,6 +295,8 @@ GroupedPlan grouped_plan(int64_t T, int64_t E, int64_t N, int64_t K, ql_format f
     g.plan.ks = 1;
     if (!is_decode(cfg)) g.plan.cps = int(L.kchunks);
     g.ws_bytes = round256(size_t(E + 1) * 4) + round256(size_t(g.plan.mtiles) * 8);
+    g.fits = is_decode(cfg) ? (g.plan.mtiles <= GRID_YZ_MAX)
+                            : (int64_t(g.plan.mtiles) * g.plan.nblocks <= GRID_X_MAX);
     return g;
 }
 
@@ -420,7 +435,9 @@ ql_status qlinear_grouped_workspace_bytes(ql_format f, int64_t T, int64_t E, int
         *bytes = 0;
         return QL_OK;
     }
-    *bytes = grouped_plan(T, E, N, K, f, group).ws_bytes;
+    const GroupedPlan gp = grouped_plan(T, E, N, K, f, group);
+    if (!gp.fits) return QL_E_SHAPE;
+    *bytes = gp.ws_bytes;
     return QL_OK;
 }
 
@@ -442,6 +459,7 @@ ql_status qlinear_grouped_forward(const void *x, int64_t T, const int32_t *token
     if (!aligned(out, out_dtype == QL_F32 ? 4 : 2)) return QL_E_ALIGN;
     const Layout L = layout_of(f, N, K, group, has_zeros);
     const GroupedPlan gp = grouped_plan(T, E, N, K, f, group);
+    if (!gp.fits) return QL_E_SHAPE;
     if (!workspace || workspace_bytes < gp.ws_bytes) return QL_E_WORKSPACE;
     if (!aligned(workspace, 256)) return QL_E_ALIGN;
     int *offsets = static_cast<int *>(workspace);

@@ -249,6 +249,9 @@ ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K,
  *           schedules split the input dimension over the wavefronts of one workgroup
  *           and take splits 0 or 1; they serve M <= 16 only (QL_E_UNSUPPORTED
  *           otherwise)
+ * A schedule whose launch grid exceeds the device's limits (more than 65535 splits, or
+ * more than 65535 row blocks for the tiles that take the row blocks as the grid's
+ * second dimension) is refused with QL_E_UNSUPPORTED before any launch.
  */
 typedef struct ql_schedule {
     int32_t tile;
@@ -330,8 +333,10 @@ ql_status qlinear_forward_a8(const void *x, int64_t M, int64_t N, int64_t K, con
  *   workspace          qlinear_grouped_workspace_bytes() bytes, 256-byte aligned (the
  *                      expert offsets and the tile map are written there)
  * The kernels are those of qlinear_forward(): the decode kernel in slots of 16 rows when
- * the experts average at most 16 tokens, else the LDS-ring tiles; each workgroup takes one
- * row block of one expert.  T = 0 or E = 0 is a no-op.
+ * the experts average at most 16 tokens (and ceil(T / 16) + E <= 65535, the grid
+ * dimension that holds the slots), else the LDS-ring tiles; each workgroup takes one
+ * row block of one expert.  T = 0 or E = 0 is a no-op.  Shapes whose grid would exceed
+ * 2^31 - 1 workgroups are refused with QL_E_SHAPE by both functions.
  */
 ql_status qlinear_grouped_workspace_bytes(ql_format f, int64_t T, int64_t E, int64_t N, int64_t K,
                                           int group, size_t *bytes);

@@ -225,6 +225,50 @@ def test_schedule_entry_points(L):
     assert L.qlinear_workspace_bytes_ex(INT4, 8, 4096, 4096, 128, 0, ctypes.byref(dec2), ctypes.byref(b)) == 4
 
 
+def test_launch_grid_limits(L):
+    """Schedules whose launch grid exceeds the device's limits (65535 along the second
+    and third grid dimensions, 2^31 - 1 along the first) are refused before any launch."""
+    import bit_weight_only_offline_amd as Q
+    Sched = Q.Schedule
+    b = ctypes.c_size_t()
+    r, c, k = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    n = L.qlinear_num_tiles()
+    kinds = []
+    for t in range(n):
+        L.qlinear_tile_shape(t, ctypes.byref(r), ctypes.byref(c), ctypes.byref(k))
+        kinds.append((t, r.value, c.value, k.value))
+    ring = [t for t, rows, cols, kb in kinds if kb == 128][0]   # a ring tile (one chunk per stage)
+    # splits along the grid's second dimension: 65535 are accepted, 65536 are not
+    K = 65536 * 128
+    ok = Sched(ring, 65535)
+    assert L.qlinear_workspace_bytes_ex(CB4, 1, 16, K, 0, 0, ctypes.byref(ok), ctypes.byref(b)) == QL_OK
+    over = Sched(ring, 65536)
+    assert L.qlinear_workspace_bytes_ex(CB4, 1, 16, K, 0, 0, ctypes.byref(over), ctypes.byref(b)) == QL_E_UNSUPPORTED
+    assert L.qlinear_forward_ex(FAKE, 1, 16, K, FAKE, FAKE, FAKE, CB4, 0, 0, None, 0, FAKE, 0, FAKE, 1 << 40,
+                                ctypes.byref(over), None) == QL_E_UNSUPPORTED
+    # tiles whose row blocks are the grid's second dimension: 65536 row blocks are refused
+    kind1 = [(t, rows) for t, rows, cols, kb in kinds if kb > 128]
+    if kind1:
+        t, rows = kind1[0]
+        s1 = Sched(t, 1)
+        assert L.qlinear_workspace_bytes_ex(INT4, 65535 * rows, 16, 128, 128, 0, ctypes.byref(s1),
+                                            ctypes.byref(b)) == QL_OK
+        assert L.qlinear_workspace_bytes_ex(INT4, 65536 * rows, 16, 128, 128, 0, ctypes.byref(s1),
+                                            ctypes.byref(b)) == QL_E_UNSUPPORTED
+    # grouped: ceil(T/16) + E decode slots past 65535 are served by the 32-row ring tile,
+    # whose slot map (ceil(T/32) + E pairs of int32) sizes the workspace
+    T = E = 70000
+    assert L.qlinear_grouped_workspace_bytes(INT4, T, E, 16, 128, 128, ctypes.byref(b)) == QL_OK
+    r256 = lambda v: (v + 255) // 256 * 256
+    assert b.value == r256((E + 1) * 4) + r256(((T + 31) // 32 + E) * 8)
+    T = E = 20000                                        # decode slots fit: 16-row slots
+    assert L.qlinear_grouped_workspace_bytes(INT4, T, E, 16, 128, 128, ctypes.byref(b)) == QL_OK
+    assert b.value == r256((E + 1) * 4) + r256(((T + 15) // 16 + E) * 8)
+    # a ring grid of more than 2^31 - 1 workgroups
+    assert L.qlinear_grouped_workspace_bytes(MXFP4, (1 << 31) - 1, 1, 1 << 20, 128, 32,
+                                             ctypes.byref(b)) == QL_E_SHAPE
+
+
 def test_int8_addmm_validation_before_launch(L):
     def a(N=64, K=256, G=256, w=FAKE, s=FAKE, m1=FAKE, m2=FAKE, r=8, alpha=1.0, beta=1.0, st=0, seed=0):
         return L.qlinear_int8_addmm(N, K, G, w, s, m1, m2, r, ctypes.c_float(alpha), ctypes.c_float(beta), st,

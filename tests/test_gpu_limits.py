@@ -114,3 +114,38 @@ def test_largest_int8_weight():
     # a weight one column tile larger does not fit 32-bit offsets: refused
     with pytest.raises(Q.QLinearError):
         Q.packed_bytes("int8", N + 16, K, G)
+
+
+def test_grouped_many_experts_past_decode_grid():
+    """70000 experts with one token each: the ceil(T/16) + E slots of the decode kernel
+    exceed the grid's second dimension (65535), so the 32-row ring tile serves, with its
+    slots along the first.  Sampled tokens against the oracle, each with its own expert."""
+    Q = _lib()
+    E = T = 70000
+    N, K, G = 16, 128, 128
+    print(f"limits: grouped int4 E={E} T={T} N={N} K={K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(43)
+    codes = torch.randint(0, 256, (E * N, K // 2), generator=g, device="cuda", dtype=torch.uint8)
+    scales = (torch.rand((E * N, K // G), generator=g, device="cuda") * 0.02 + 1e-3).to(torch.float16)
+    pe = Q.pack_experts("int4", N, K, G, [(codes[e * N:(e + 1) * N], scales[e * N:(e + 1) * N], None)
+                                          for e in range(E)])
+    x = torch.randn((T, K), generator=g, device="cuda", dtype=torch.bfloat16)
+    counts = torch.ones(E, dtype=torch.int32, device="cuda")
+    y32 = Q.grouped_linear(x, pe, counts, out_dtype=torch.float32)
+    y16 = Q.grouped_linear(x, pe, counts)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y32).all()
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16)), "G3"
+
+    rng = np.random.default_rng(43)
+    tokens = np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], rng.integers(0, T, 20)]))
+    refs, gots = [], []
+    for t in tokens:
+        canon = {"codes": codes[t * N:(t + 1) * N].cpu().numpy(), "scales": scales[t * N:(t + 1) * N].cpu().numpy(),
+                 "zeros": None, "group": G}
+        refs.append(O.forward("int4", x[t:t + 1].float().cpu().numpy(), canon, K)[0])
+        gots.append(y32[t].cpu().numpy().astype(np.float64))
+    ref, got = np.array(refs), np.array(gots)
+    err = float(np.max(np.abs(got - ref))) / float(np.sqrt(np.mean(ref ** 2)))
+    print(f"  sampled {ref.size} outputs: max|dY|/rms = {err:.3e}", flush=True)
+    assert err <= TOL
