@@ -408,6 +408,20 @@ def main():
                                           "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1)}
             del pl
             torch.cuda.empty_cache()
+        # the other weight formats at the codebook prefill's shape (3072 x 3072, M = 2048),
+        # default schedules, weights from a pool as above
+        xp = torch.from_numpy(S.activations(wl5, 2048)).cuda().to(torch.bfloat16)
+        for fmt, G, sym in (("int4", 128, True), ("int4", 128, False), ("mxfp4", 32, True), ("int8", 256, True)):
+            pl = _pool(Q, fmt, wl5["N"], wl5["K"], G, sym, 8, POOL_BYTES)
+            ms, _ = time_forward(Q, pl, xp, None, max(20, len(pl), args.steps // 4), 5, use_graph,
+                                 warm_s=AUX_WARM_S, reps=3)
+            fl = 2.0 * 2048 * wl5["N"] * wl5["K"]
+            tf = fl / (ms * 1e-3) / 1e12
+            others[f"{fmt}{'' if sym else '_asym'}_g{G}_3072/M2048"] = {
+                "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+            del pl
+            torch.cuda.empty_cache()
+        del xp
 
     moe = {}
     if args.sweep:
