@@ -47,7 +47,7 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
 
 template <int FMT, bool ZP, int GS>
 hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
-    static_assert(NUM_TILE_CFGS == 21, "one case per compiled schedule");
+    static_assert(NUM_TILE_CFGS == 22, "one case per compiled schedule");
     switch (p.cfg) {
         case 0: return launch_one<FMT, ZP, GS, 0>(p, a, st);
         case 1: return launch_one<FMT, ZP, GS, 1>(p, a, st);
@@ -70,6 +70,7 @@ hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
         case 18: return launch_one<FMT, ZP, GS, 18>(p, a, st);
         case 19: return launch_one<FMT, ZP, GS, 19>(p, a, st);
         case 20: return launch_one<FMT, ZP, GS, 20>(p, a, st);
+        case 21: return launch_one<FMT, ZP, GS, 21>(p, a, st);
         default: return hipErrorInvalidValue;
     }
 }
