@@ -238,12 +238,14 @@ inline int default_cfg(const Layout &L, int64_t M) {
     if (M <= 16) return decode_cfg(L.ntiles);
     if (M <= 64) return 12;
     const bool intf = L.fmt == FMT_INT4 || L.fmt == FMT_INT8;
-    if (M <= 256) {
+    // weights streamed from HBM (16 MiB and more) take 64 x 256 tiles up to M = 1024:
+    // with a two-deep ring (measured 1.3-1.9x faster than 64 x 192 at M = 128-256 and
+    // up to 1.35x faster than 128 x 192 at M = 512-1024, from 29 MB up), INT8 with its
+    // four-deep ring; smaller, cache-resident weights keep 64 x 192 up to M = 256
+    const bool streamed = L.w_bytes >= (size_t(16) << 20);
+    if (M <= 256 || (streamed && M <= 1024)) {
         if (L.fmt == FMT_INT8) return 15;
-        // weights streamed from HBM (16 MiB and more): 64 x 256 tiles with a two-deep ring
-        // (measured 1.3-1.9x faster than 64 x 192 from 29 MB up); smaller, cache-resident
-        // weights keep 64 x 192
-        return L.w_bytes >= (size_t(16) << 20) ? 21 : 16;
+        return streamed ? 21 : 16;
     }
     if (L.fmt == FMT_INT8) return 13;
     return intf ? 8 : 13;

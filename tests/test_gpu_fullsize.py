@@ -25,7 +25,7 @@ TOL = 1e-2
 
 WORKLOADS = [
     ("int4_asym_decode", (1, 4, 8, 16)),
-    ("mxfp4_up", (1, 16, 64, 128)),        # M = 128, 256: the schedule of HBM-streamed weights
+    ("mxfp4_up", (1, 16, 64, 128, 512)),   # M = 128-512: the schedule of HBM-streamed weights
     ("mxfp4_down", (1, 16, 64, 256)),
     ("int8_swiglu", (1, 16, 128)),
     ("cb4_prefill", (256, 2048)),
