@@ -151,10 +151,12 @@ def summarize_trace(d):
     for r in rows:
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         agg.setdefault(r["Kernel_Name"], []).append(dur)
-    lines = [f"{'calls':>6} {'avg_us':>9} {'median_us':>9} {'min_us':>8} {'max_us':>8}  kernel"]
+    lines = [f"{'calls':>6} {'avg_us':>9} {'median_us':>9} {'p95_us':>8} {'min_us':>8} {'max_us':>8}  kernel"]
     for name, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         v = sorted(v)
-        lines.append(f"{len(v):6d} {sum(v) / len(v):9.3f} {v[len(v) // 2]:9.3f} {v[0]:8.3f} {v[-1]:8.3f}  {name}")
+        p95 = v[min(len(v) - 1, int(np.ceil(0.95 * len(v))) - 1)]
+        lines.append(f"{len(v):6d} {sum(v) / len(v):9.3f} {v[len(v) // 2]:9.3f} {p95:8.3f} {v[0]:8.3f} {v[-1]:8.3f}  "
+                     f"{name}")
     return "\n".join(lines)
 
 
