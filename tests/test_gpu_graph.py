@@ -187,3 +187,50 @@ def test_quantize_replays_match_eager(fmt, G, sym):
         _same(outs[1], ref[1])
         if fmt == "int4":
             _same(outs[2], ref[2])
+
+
+_CAPTURE_FIRST = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import torch
+import bit_weight_only_offline_amd as Q
+import synthetic as S
+from helpers import quantize, to_device
+
+N, K, M = 200, 640, 300
+w = (np.random.default_rng(5).standard_normal((N, K)) * 0.02).astype(np.float32)
+pw = Q.pack("mxfp4", N, K, 32, *to_device("mxfp4", quantize("mxfp4", w, 32)))
+x = torch.from_numpy(S.to_bf16_values(np.random.default_rng(6).standard_normal((M, K)).astype(np.float32))).cuda()
+x = x.to(torch.bfloat16)
+out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+ws = torch.zeros(max(Q.workspace_bytes("mxfp4", M, N, K, 32, None, (13, 2)), 256), dtype=torch.uint8, device="cuda")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):            # the first forward of this process, inside the capture
+    Q.linear(x, pw, out_dtype=torch.float32, out=out, workspace=ws, schedule=(13, 2))
+for _ in range(3):
+    out.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    ref = Q.linear(x, pw, out_dtype=torch.float32, schedule=(13, 2))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "replay differs from the eager call"
+print("capture-first ok", flush=True)
+"""
+
+
+def test_first_call_inside_a_capture():
+    """A process whose very first forward (here a ring schedule with a split, so the
+    kernel's dynamic-LDS limit is raised and a reduce kernel runs) happens inside a
+    graph capture: the capture succeeds and every replay equals the eager call."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ)
+    env["PYTHONPATH"] = os.pathsep.join([root, os.path.join(root, "tests"), env.get("PYTHONPATH", "")])
+    r = subprocess.run([sys.executable, "-c", _CAPTURE_FIRST, root], capture_output=True, text=True, timeout=240,
+                       env=env)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    assert r.returncode == 0 and "capture-first ok" in r.stdout
