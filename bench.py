@@ -423,6 +423,40 @@ def main():
                 "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
             del pl
             torch.cuda.empty_cache()
+        # context, not this library: torch's dense bf16 product (hipBLASLt) at the same
+        # shape, a pool of contiguous [K, N] weights cycled like the packed ones
+        wt = torch.randn(wl5["K"], wl5["N"], device="cuda").to(torch.bfloat16)
+        dense = [wt] + [wt.clone() for _ in range(max(0, int(np.ceil(POOL_BYTES / (wt.numel() * 2))) - 1))]
+        yd = torch.empty((2048, wl5["N"]), dtype=torch.bfloat16, device="cuda")
+        steps_d = max(20, len(dense))
+        for i in range(5):
+            torch.matmul(xp, dense[i % len(dense)], out=yd)
+        torch.cuda.synchronize()
+        gd, sd = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        sd.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(sd):
+            with torch.cuda.graph(gd, stream=sd):
+                for i in range(steps_d):
+                    torch.matmul(xp, dense[i % len(dense)], out=yd)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < AUX_WARM_S:
+            gd.replay()
+            torch.cuda.synchronize()
+        tds = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gd.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            tds.append(e0.elapsed_time(e1) / steps_d)
+        msd = sorted(tds)[1]
+        fl = 2.0 * 2048 * wl5["N"] * wl5["K"]
+        others["torch_bf16_matmul_3072/M2048"] = {"us": round(msd * 1e3, 2), "TFLOP/s": round(fl / (msd * 1e-3) / 1e12, 1),
+                                                  "mfma_frac": round(fl / (msd * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del gd, dense, wt, yd
+        torch.cuda.empty_cache()
         del xp
 
     moe = {}
