@@ -450,18 +450,12 @@ def output_rows(fmt: str, x, canon: dict, K: int, rows, cols, bias=None, swiglu=
     return out
 
 
-def canonical_bytes(fmt: str, N: int, K: int, group: int = 128, zeros: bool = False) -> dict:
-    """Storage of the canonical weight path (the accounting of the OrbitQuant card,
-    section "Benchmark": packed indices + row norms + centroids)."""
-    if fmt == "cb4":
-        return dict(codes=N * K // 2, scales=2 * N, aux=4 * 16)
-    if fmt == "int4":
-        return dict(codes=N * K // 2, scales=2 * N * (K // group), aux=(N * (K // group) + 1) // 2 if zeros else 0)
-    if fmt == "mxfp4":
-        return dict(codes=N * K // 2, scales=N * (K // 32), aux=0)
-    if fmt == "int8":
-        return dict(codes=N * K, scales=2 * N * (K // group), aux=0)
-    raise ValueError(fmt)
+def canonical_bytes(fmt: str, N: int, K: int) -> dict:
+    """Storage of the codebook weight path (the accounting of the OrbitQuant card, section
+    "Benchmark": packed indices + row norms + centroids)."""
+    if fmt != "cb4":
+        raise ValueError(fmt)
+    return dict(codes=N * K // 2, scales=2 * N, aux=4 * 16)
 
 
 # --------------------------------------------------------------------------------------
