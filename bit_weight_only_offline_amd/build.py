@@ -17,17 +17,18 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlinear.so")
 
-SOURCES = [
-    "ql_api.hip",
-    "ql_pack.hip",
+SOURCES = [   # slowest first, so the parallel build starts them first
+    "ql_gemm_int4_zp.hip",
     "ql_gemm_int4.hip",
     "ql_gemm_int8.hip",
-    "ql_gemm_mxfp4.hip",
     "ql_gemm_cb4.hip",
+    "ql_gemm_mxfp4.hip",
+    "ql_gemm_a8.hip",
+    "ql_api.hip",
+    "ql_pack.hip",
     "ql_misc.hip",
     "ql_quant.hip",
     "ql_lora.hip",
-    "ql_gemm_a8.hip",
 ]
 
 ARCH = "gfx950"

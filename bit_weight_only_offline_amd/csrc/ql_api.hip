@@ -232,7 +232,7 @@ ql_status qlinear_tile_shape(int tile, int *rows, int *cols, int *kblock) {
     const TileCfg &t = TILE_CFGS[tile];
     *rows = cfg_rows(t);
     *cols = 16 * cfg_ntiles(t);
-    *kblock = t.kind == 0 ? 0 : (t.kind == 1 ? t.SK : 128);   // 0: no activation staging
+    *kblock = t.kind == 0 ? 0 : chunk_k(FMT_INT4);   // 0: no activation staging (decode)
     return QL_OK;
 }
 
@@ -259,11 +259,10 @@ ql_status plan_for(ql_format f, int64_t M, int64_t N, int64_t K, int group, int 
     }
     if (is_decode(cfg) && (M > 16 || splits > 1)) return QL_E_UNSUPPORTED;   // decode: M <= 16, no split
     *p = make_plan(*L, M, cfg, splits, PLAN_CUS, act == QL_ACT_SWIGLU);
-    // grid: decode (column blocks); ring tiles (row x column blocks, splits); tiles of
-    // kind 1 (column blocks, row blocks, splits)
+    // grid: decode (column blocks); ring tiles (row x column blocks, splits)
     const int kind = TILE_CFGS[cfg].kind;
     const int64_t gx = kind == 2 ? int64_t(p->mtiles) * p->nblocks : int64_t(p->nblocks);
-    if (gx > GRID_X_MAX || p->ks > GRID_YZ_MAX || (kind == 1 && p->mtiles > GRID_YZ_MAX)) return QL_E_UNSUPPORTED;
+    if (gx > GRID_X_MAX || p->ks > GRID_YZ_MAX) return QL_E_UNSUPPORTED;
     return QL_OK;
 }
 
@@ -391,7 +390,7 @@ ql_status qlinear_forward_ex(const void *x, int64_t M, int64_t N, int64_t K, con
     a.ngroups = int(L.ngroups);
     a.cps = p.cps;
     a.ks = p.ks;
-    a.swiglu = (act == QL_ACT_SWIGLU && p.fuse_swiglu) ? 1 : 0;
+    a.swiglu = (act == QL_ACT_SWIGLU && p.fuse_swiglu) ? 1 : 0;   // the kernel forms h itself
     a.out_f32 = out_dtype == QL_F32 ? 1 : 0;
     a.w_bytes = uint32_t(L.w_bytes);
     a.s_bytes = uint32_t(L.s_bytes);

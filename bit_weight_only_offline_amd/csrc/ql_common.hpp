@@ -121,20 +121,18 @@ struct GemmArgs {
 // Schedules compiled into the library.
 //   kind 0 (decode, M <= 16): one workgroup per 16*NT output columns over the whole
 //           input dimension, split over WK wavefronts and reduced in LDS;
-//   kind 1 (tiles): 4 wavefronts side by side cover 16*MT rows x 64*NT columns, the
-//           activations staged through LDS in blocks of SK inputs; the input
-//           dimension may be split over workgroups (then a reduce kernel adds the
-//           partial sums in split order).
 //   kind 2 (LDS ring): WM x WN wavefronts, each 16*MT rows x 16*NT columns, times WK
 //           wavefronts that share a tile and split each chunk's k-steps; activations
 //           and packed weights staged chunk by chunk into a PF-deep LDS ring by direct
-//           buffer->LDS loads (ql_gemm_lds.hpp); split-K as for kind 1.
-// PF = weight chunks in flight per wavefront (kinds 0, 1) or ring depth (kind 2).
+//           buffer->LDS loads (ql_gemm_lds.hpp); the input dimension may be split over
+//           workgroups (then a reduce kernel adds the partial sums in split order).
+// PF = weight chunks in flight per wavefront (kind 0) or ring depth (kind 2); SK is
+// unused (kept so every entry has the same fields).
 struct TileCfg { int kind, MT, NT, SK, PF, WK, WM, WN; };
 constexpr int NUM_TILE_CFGS = 22;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {0, 1, 1, 0, 4, 8, 1, 1}, {0, 1, 2, 0, 4, 8, 1, 1}, {0, 1, 4, 0, 4, 4, 1, 1}, {0, 1, 1, 0, 8, 4, 1, 1},
-    {1, 2, 2, 512, 4, 4, 1, 4}, {1, 4, 2, 256, 4, 4, 1, 4}, {1, 8, 2, 128, 2, 4, 1, 4}, {1, 8, 1, 128, 4, 4, 1, 4},
+    {2, 2, 3, 0, 4, 2, 1, 2}, {2, 1, 3, 0, 4, 2, 2, 2}, {2, 1, 3, 0, 4, 1, 2, 2}, {2, 2, 3, 0, 4, 1, 1, 4},
     {2, 8, 3, 0, 3, 1, 1, 4}, {2, 8, 4, 0, 3, 1, 1, 4}, {2, 4, 4, 0, 3, 1, 2, 2}, {2, 4, 3, 0, 4, 1, 1, 4},
     {2, 2, 4, 0, 4, 1, 1, 4}, {2, 8, 3, 0, 3, 2, 1, 4}, {2, 8, 4, 0, 3, 2, 1, 4}, {2, 4, 4, 0, 4, 2, 1, 4},
     {2, 4, 3, 0, 4, 2, 1, 4}, {2, 2, 4, 0, 6, 1, 1, 4}, {2, 4, 3, 0, 5, 1, 1, 4},
@@ -144,12 +142,12 @@ constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.
 __host__ __device__ constexpr int cfg_rows(const TileCfg &t) { return 16 * t.MT * (t.kind == 2 ? t.WM : 1); }
-__host__ __device__ constexpr int cfg_ntiles(const TileCfg &t) {
-    return t.kind == 0 ? t.NT : (t.kind == 1 ? 4 * t.NT : t.NT * t.WN);
-}
+__host__ __device__ constexpr int cfg_ntiles(const TileCfg &t) { return t.kind == 0 ? t.NT : t.NT * t.WN; }
 // One stage of a decode wavefront's LDS ring: NT packed weight tiles, the chunk's
 // scale words and zero-point words (256-byte blocks), then the activation block of 16
-// rows x one chunk of bf16.
+// rows x one chunk of bf16; with the fused SwiGLU input stage (sw), one more 1 KiB
+// block for the gate rows (the up rows go to the activation block, where h replaces
+// them).
 __host__ __device__ constexpr int gemv_spc(int fmt, int gs) {
     return (fmt == FMT_INT4 || fmt == FMT_INT8) ? (gs <= chunk_k(fmt) / 32 ? chunk_k(fmt) / 32 / gs : 1) : 1;
 }
@@ -160,19 +158,19 @@ __host__ __device__ constexpr int gemv_scale_blocks(int fmt, int gs, int nt) {
 __host__ __device__ constexpr int gemv_zero_blocks(int fmt, bool zp, int gs, int nt) {
     return (fmt == FMT_INT4 && zp) ? (nt * gemv_spc(fmt, gs) * 2 + 63) / 64 : 0;
 }
-__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt) {
+__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt, bool sw = false) {
     return nt * TILE_BYTES + 256 * (gemv_scale_blocks(fmt, gs, nt) + gemv_zero_blocks(fmt, zp, gs, nt)) +
-           16 * chunk_k(fmt) * 2;
+           16 * chunk_k(fmt) * 2 + (sw ? 1024 : 0);
 }
 constexpr int LDS_BYTES_MAX = 160 * 1024;
 // ring depth: PF stages per wavefront, fewer if they would not fit the LDS
-__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf) {
-    return pf * wk * gemv_stage_bytes(fmt, zp, gs, nt) <= LDS_BYTES_MAX
+__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
+    return pf * wk * gemv_stage_bytes(fmt, zp, gs, nt, sw) <= LDS_BYTES_MAX
                ? pf
-               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt));
+               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt, sw));
 }
-__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf) {
-    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf) * gemv_stage_bytes(fmt, zp, gs, nt);
+__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
+    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf, sw) * gemv_stage_bytes(fmt, zp, gs, nt, sw);
 }
 // LDS of a ring schedule: PF stages of activations + packed tiles + every wavefront's
 // scale and zero-point words, or, when WK > 1, the hand-over of one k-half's
@@ -198,15 +196,15 @@ __host__ __device__ constexpr int ring_lds_bytes(int fmt, bool zp, int gs, int w
 struct Plan {
     int cfg = 0;          // index into TILE_CFGS
     int mtiles = 1, nblocks = 1, ks = 1, cps = 1;
-    bool fuse_swiglu = false;   // SwiGLU formed while staging activations (tile kind)
+    bool fuse_swiglu = false;   // the decode kernel forms h from the raw input itself
     size_t ws_h = 0;            // bytes of the materialised SwiGLU input at offset 0
     size_t ws_bytes = 0;        // ws_h + split-K partial sums
 };
 
-// A tile workgroup recomputes silu for its own rows and input range, so fused SwiGLU
-// costs (column blocks) x M x K evaluations; beyond a couple of column blocks one
-// prologue pass that materialises h is cheaper.
-constexpr int FUSE_SWIGLU_MAX_NBLOCKS = 2;
+// The decode kernel forms the SwiGLU input h itself when M is at most this: every
+// workgroup then evaluates silu over the whole input dimension for the batch's rows,
+// which costs less than a separate pass over the raw input only while the rows are few.
+constexpr int SWIGLU_FUSE_MAX_M = 2;
 
 inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 
@@ -269,7 +267,8 @@ inline Plan make_plan(const Layout &L, int64_t M, int cfg, int splits, int num_c
         cpw = ceil_div(cpw, span) * span;
         p.cps = int(cpw);
         p.ks = 1;
-        if (swiglu) p.ws_h = round256(size_t(M) * size_t(L.K) * 2);
+        p.fuse_swiglu = swiglu && M <= SWIGLU_FUSE_MAX_M;
+        if (swiglu && !p.fuse_swiglu) p.ws_h = round256(size_t(M) * size_t(L.K) * 2);
         p.ws_bytes = p.ws_h;
         return p;
     }
@@ -281,7 +280,7 @@ inline Plan make_plan(const Layout &L, int64_t M, int cfg, int splits, int num_c
         // enough workgroups to give every compute unit one (a machine already three
         // quarters full is not split: the split costs a reduce pass)
         ks = 4 * wgs < 3 * int64_t(num_cu) ? ceil_div(num_cu, wgs) : 1;
-        const int64_t blk = std::max<int64_t>(span, t.kind == 1 ? t.SK / ch : 2);
+        const int64_t blk = std::max<int64_t>(span, 2);
         ks = std::min<int64_t>(ks, std::max<int64_t>(1, L.kchunks / blk));
     }
     ks = std::max<int64_t>(1, std::min<int64_t>(ks, L.kchunks));
@@ -290,8 +289,7 @@ inline Plan make_plan(const Layout &L, int64_t M, int cfg, int splits, int num_c
     ks = ceil_div(L.kchunks, cps);
     p.ks = int(ks);
     p.cps = int(cps);
-    p.fuse_swiglu = swiglu && t.kind == 1 && p.nblocks <= FUSE_SWIGLU_MAX_NBLOCKS;
-    if (swiglu && !p.fuse_swiglu) p.ws_h = round256(size_t(M) * size_t(L.K) * 2);
+    if (swiglu) p.ws_h = round256(size_t(M) * size_t(L.K) * 2);
     p.ws_bytes = p.ws_h + (ks > 1 ? round256(size_t(ks) * size_t(M) * size_t(L.Np) * 4) : 0);
     return p;
 }

@@ -7,10 +7,12 @@
 //          in the decode kernel (where one fewer operation per value matters more than
 //          the extra activation-sum MFMA)              (byte -> f32 -> bf16)
 //   MXFP4  E2M1 code with its E8M0 scale  ->  bf16(e2m1 * 2^(e-127))  (hardware convert)
-//   CB4    sign-magnitude index           ->  +-bf16(alpha * c[8 + m])  (byte permutes)
+//   CB4    sign-magnitude index           ->  +-bf16(alpha * c[8 + m])  (byte permutes),
+//          and with the two-term operand also +-bf16(alpha * c[8 + m] - that), a second
+//          operand for a second MFMA, so the two together carry ~16 bits of the level
 // INT4's offset (128, plus 8 or its zero-point), group scales and codebook row scales are
 // applied to the float32 accumulators, so no rounding happens before the matrix cores except the
-// single bf16 rounding of alpha * c for the codebook.
+// bf16 rounding of alpha * c (one or two terms) for the codebook.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -185,9 +187,10 @@ __device__ inline u32x4 dec_int8(uint32_t d0, uint32_t d1) {
     return r;
 }
 
-// ---- MXFP4: E8M0 code -> float32 scale 2^(e-127); code 0 is the subnormal 2^-127 -------
+// ---- MXFP4: E8M0 code -> float32 scale 2^(e-127); code 0 is the subnormal 2^-127 and
+// code 255 is NaN (a quiet-NaN mantissa bit, set only when e + 1 carries into bit 8) -----
 __device__ inline float e8m0_to_f32(uint32_t e) {
-    return __uint_as_float(e ? (e << 23) : 0x00400000u);
+    return __uint_as_float(e ? (e << 23) | (((e + 1u) >> 8) << 22) : 0x00400000u);
 }
 
 __device__ inline u32x4 dec_mxfp4(uint32_t w, float scale) {
@@ -223,16 +226,20 @@ __device__ inline u32x4 dec_cb4(uint32_t w, const CbLut &L) {
 }
 
 // Codebook record (128 bytes) written by the packer:
-//   [0, 64)   float32 centroids c[16] as given
-//   [64, 80)  CbLut planes of bf16(alpha * c[8 + m]), m = 0..7
-//   [80, 84)  float32 1/alpha
-//   [84, 88)  float32 alpha
+//   [0, 64)    float32 centroids c[16] as given
+//   [64, 80)   CbLut planes of hi_m = bf16(alpha * c[8 + m]), m = 0..7
+//   [80, 84)   float32 1/alpha
+//   [84, 88)   float32 alpha
+//   [88, 104)  CbLut planes of lo_m = bf16(fp32(alpha * c[8 + m]) - hi_m)
+//   [104, 108) split: 1 = the kernels use the two-term operand hi + lo
 struct CbRecord {
     float centroids[16];
     CbLut lut;
     float inv_alpha;
     float alpha;
-    uint32_t pad[10];
+    CbLut lut_lo;
+    uint32_t split;
+    uint32_t pad[5];
 };
 static_assert(sizeof(CbRecord) == CB_AUX_BYTES, "codebook record size");
 

@@ -1,7 +1,8 @@
 // Selects the compiled tile shape of the linear kernel for one format.
 #pragma once
 
-#include "ql_gemm.hpp"
+#include <type_traits>
+
 #include "ql_gemv.hpp"
 #include "ql_gemm_lds.hpp"
 
@@ -20,13 +21,20 @@ template <int FMT, bool ZP, int GS, int I>
 hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
     constexpr TileCfg t = TILE_CFGS[I];
     if constexpr (t.kind == 0) {
-        auto kern = qgemv_kernel<FMT, ZP, GS, t.NT, t.WK, t.PF>;
-        constexpr size_t lds = gemv_lds_bytes(FMT, ZP, GS, t.NT, t.WK, t.PF);
-        static bool attr_set = false;
-        hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
+        auto go = [&](auto sw) {
+            constexpr bool SW = decltype(sw)::value;
+            auto kern = qgemv_kernel<FMT, ZP, GS, t.NT, t.WK, t.PF, SW>;
+            constexpr size_t lds = gemv_lds_bytes(FMT, ZP, GS, t.NT, t.WK, t.PF, SW);
+            static bool attr_set = false;
+            hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(p.nblocks, a.tile_map ? a.slots : 1), dim3(64 * t.WK), lds, st, a);
+            return hipSuccess;
+        };
+        hipError_t e = p.fuse_swiglu ? go(std::true_type{}) : go(std::false_type{});
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(p.nblocks, a.tile_map ? a.slots : 1), dim3(64 * t.WK), lds, st, a);
-    } else if constexpr (t.kind == 2) {
+    } else {
+        static_assert(t.kind == 2, "decode or LDS-ring schedule");
         constexpr int depth = ring_depth(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, t.PF);
         auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth>;
         constexpr size_t lds = ring_lds_bytes(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth);
@@ -35,12 +43,6 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
         hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(p.mtiles * p.nblocks, p.ks), dim3(64 * t.WM * t.WN * t.WK), lds, st, a);
-    } else {
-        const dim3 grid(p.nblocks, p.mtiles, p.ks);
-        if (p.fuse_swiglu)
-            hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, t.MT, t.NT, t.SK, t.PF, true>), grid, dim3(WG_THREADS), 0, st, a);
-        else
-            hipLaunchKernelGGL((qmm_kernel<FMT, ZP, GS, t.MT, t.NT, t.SK, t.PF, false>), grid, dim3(WG_THREADS), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -22,7 +22,8 @@
 // and every wait is explicit.  Out-of-range
 // rows and inputs load as zero (ranged buffer loads).  Workgroups are numbered so that
 // the ones sharing activation rows run on the same XCD (blocks are dealt round-robin to
-// the 8 XCDs, each with its own L2).
+// the 8 XCDs, each with its own L2).  Codebook weights packed with the two-term operand
+// (the record's split flag) issue a second MFMA per fragment on the residual operand.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -64,7 +65,6 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     static_assert(STAGE == ring_stage_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW), "stage layout");
     constexpr int NA = A_BYTES / 1024;              // wave-wide A loads per stage
     constexpr int NB = NTT;                         // wave-wide B loads per stage
-    static_assert(NA % W == 0, "activation loads split evenly over the wavefronts");
 
     static_assert(S >= 2 && S <= 6, "ring depth");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -73,11 +73,13 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kh = WKK == 1 ? 0 : wv / (WM * WN);  // which k-steps of each chunk
     const int wm = (wv % (WM * WN)) / WN, wn = wv % WN;
-    // B tiles are dealt round-robin, every wavefront issuing NBW loads: tile (wv + W q) mod
-    // NB, so when W does not divide NB a few tiles are fetched twice (identical bytes to
-    // the same LDS slot) and every wavefront waits for the same count
+    // A loads and B tiles are dealt round-robin, every wavefront issuing NAW and NBW
+    // loads: load (wv + W q) mod NA (NB), so when W does not divide NA (NB) a few are
+    // fetched twice (identical bytes to the same LDS slot) and every wavefront waits for
+    // the same count
+    constexpr int NAW = (NA + W - 1) / W;
     constexpr int NBW = (NB + W - 1) / W;
-    constexpr int PER_STAGE = NA / W + NBW + NSS + NSZ;   // vector-memory loads per wavefront per stage
+    constexpr int PER_STAGE = NAW + NBW + NSS + NSZ;   // vector-memory loads per wavefront per stage
     const int g = lane >> 4, c = lane & 15;
 
     // XCD-aware numbering: block b runs on XCD b % 8; give each XCD a contiguous range of
@@ -131,8 +133,14 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     const uint32_t s_shift = 16u * (c & 1);
     const uint32_t z_shift = 8u * ((c >> 1) & 3) + 4u * (c & 1);
 
-    CbLut lut = {0u, 0u, 0u, 0u};
-    if (FMT == FMT_CB4) lut = reinterpret_cast<const CbRecord *>(a.aux)->lut;
+    CbLut lut = {0u, 0u, 0u, 0u}, lut2 = {0u, 0u, 0u, 0u};
+    uint32_t split = 0;
+    if (FMT == FMT_CB4) {
+        const CbRecord *cr = reinterpret_cast<const CbRecord *>(a.aux);
+        lut = cr->lut;
+        lut2 = cr->lut_lo;
+        split = uint32_t(__builtin_amdgcn_readfirstlane(int(cr->split)));
+    }
 
     f32x4 acc[MTW][NTW], tmp[MTW][NTW], xs[MTW];
 #pragma unroll
@@ -148,13 +156,13 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     // per-lane parts of the ring loads that do not change from chunk to chunk: the
     // activation slot's row (rows >= M get bit 31: never fetched) and input offset, and
     // the weight tile's column block
-    uint32_t a_off[NA / W];
-    int a_k[NA / W];
+    uint32_t a_off[NAW];
+    int a_k[NAW];
 #pragma unroll
-    for (int q = 0; q < NA / W; ++q) {
+    for (int q = 0; q < NAW; ++q) {
         // load j covers rows j*RPI .. +RPI-1; this lane's row and (swizzled) piece
         using XB = XBlock<FMT>;
-        const int row = (wv + W * q) * XB::RPI + lane / XB::P;
+        const int row = ((wv + W * q) % NA) * XB::RPI + lane / XB::P;
         const int m = m0 + row;
         a_k[q] = 8 * ((lane % XB::P) ^ XB::xswz(row));
         a_off[q] = (m < a.M) ? (uint32_t(m) * uint32_t(a.ldx) + uint32_t(a_k[q])) * 2u : 0x80000000u;
@@ -192,9 +200,9 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     // ORed into the finished offset: every in-range offset is below 2^31, and a
     // past-K offset added after the mark could carry out of bit 31 and wrap back into
     // the buffer when the activations fill nearly 2 GiB
-    uint32_t tail_mask[NA / W];
+    uint32_t tail_mask[NAW];
 #pragma unroll
-    for (int q = 0; q < NA / W; ++q)
+    for (int q = 0; q < NAW; ++q)
         tail_mask[q] = ((a.kchunks - 1) * CH + a_k[q] >= a.K) ? 0x80000000u : 0u;
 
     // issue the loads of chunk i (relative) into ring buffer buf
@@ -204,8 +212,8 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
         const uint32_t kbase2 = uint32_t(kc * CH) * 2u;
         const uint32_t last = kc == a.kchunks - 1 ? 0xFFFFFFFFu : 0u;      // wave-uniform
 #pragma unroll
-        for (int q = 0; q < NA / W; ++q)
-            ld128_lds(xr, (a_off[q] + kbase2) | (tail_mask[q] & last), base + (wv + W * q) * 1024);
+        for (int q = 0; q < NAW; ++q)
+            ld128_lds(xr, (a_off[q] + kbase2) | (tail_mask[q] & last), base + ((wv + W * q) % NA) * 1024);
 #pragma unroll
         for (int q = 0; q < NBW; ++q)
             ld128_lds(wr, b_off[q] + uint32_t(kc) * TILE_BYTES, base + A_BYTES + ((wv + W * q) % NB) * 1024);
@@ -243,7 +251,8 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     constexpr int WPW = 4 / WKK;
     static_assert(WKK == 1 || WKK == 2, "one or two k-halves");
 
-    auto compute = [&](int i, int buf) {
+    auto compute = [&](int i, int buf, auto spl) {
+        constexpr bool SPLIT = decltype(spl)::value;
         const int kc = chunk_of(i);
         const uint8_t *A = lds + buf * STAGE;
         const uint8_t *Bt = A + A_BYTES;
@@ -296,7 +305,15 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 if (FMT == FMT_INT4) bw = dec_int4(wq[j][tt]);
                 else if (FMT == FMT_INT8) bw = dec_int8<true>(wq[j][2 * tt], wq[j][2 * tt + 1]);
                 else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][tt], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
-                else bw = dec_cb4(wq[j][tt], lut);
+                else {
+                    bw = dec_cb4(wq[j][tt], lut);
+                    if constexpr (SPLIT) {
+                        // the residual term first, then the leading term
+                        const bf16x8 bl = as_bf16x8(dec_cb4(wq[j][tt], lut2));
+#pragma unroll
+                        for (int mt = 0; mt < MTW; ++mt) acc[mt][j] = mfma16x16x32(af[mt], bl, acc[mt][j]);
+                    }
+                }
                 const bf16x8 bv = as_bf16x8(bw);
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt) {
@@ -350,24 +367,28 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
         if (u < nck) issue(u, u);
 
     // ---- main loop, unrolled by the ring depth so ring slots are compile-time ----
-    for (int i0 = 0; i0 < nck; i0 += S) {
+    auto main_loop = [&](auto spl) {
+        for (int i0 = 0; i0 < nck; i0 += S) {
 #pragma unroll
-        for (int u = 0; u < S; ++u) {
-            const int i = i0 + u;
-            if (i < nck) {
-                // loads issued after chunk i's: those of chunks i+1 .. min(i+S-2, nck-1)
-                const int later = min(S - 2, nck - 1 - i);
-                if (later >= 4) wait_vmcnt<4 * PER_STAGE>();
-                else if (later == 3) wait_vmcnt<3 * PER_STAGE>();
-                else if (later == 2) wait_vmcnt<2 * PER_STAGE>();
-                else if (later == 1) wait_vmcnt<PER_STAGE>();
-                else wait_vmcnt<0>();
-                ring_barrier();
-                if (i + S - 1 < nck) issue(i + S - 1, (u + S - 1) % S);
-                compute(i, u);
+            for (int u = 0; u < S; ++u) {
+                const int i = i0 + u;
+                if (i < nck) {
+                    // loads issued after chunk i's: those of chunks i+1 .. min(i+S-2, nck-1)
+                    const int later = min(S - 2, nck - 1 - i);
+                    if (later >= 4) wait_vmcnt<4 * PER_STAGE>();
+                    else if (later == 3) wait_vmcnt<3 * PER_STAGE>();
+                    else if (later == 2) wait_vmcnt<2 * PER_STAGE>();
+                    else if (later == 1) wait_vmcnt<PER_STAGE>();
+                    else wait_vmcnt<0>();
+                    ring_barrier();
+                    if (i + S - 1 < nck) issue(i + S - 1, (u + S - 1) % S);
+                    compute(i, u, spl);
+                }
             }
         }
-    }
+    };
+    if (FMT == FMT_CB4 && split) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
 
     if constexpr (WKK > 1) {
         // add the k-halves in a fixed order: the wavefronts of the second half hand their

@@ -14,16 +14,29 @@
 // end the WK partial tiles are added in LDS in wavefront order -- a fixed order -- and
 // the epilogue applies the codebook row scale and the bias and rounds to bf16.  No
 // workspace, no cross-workgroup traffic.
+//
+// Fused SwiGLU input stage (SW, batches of at most SWIGLU_FUSE_MAX_M rows): the stage
+// receives the up rows in the activation block and the gate rows in one more block, and
+// the wavefront replaces each up value by h = bf16(up * silu(gate)) in LDS before it
+// reads its A fragments -- the same arithmetic as the prologue kernel that materialises
+// h for larger batches, so the two paths give the same linear.  Only the batch's rows
+// are evaluated, 64 lanes across one chunk of them.
+//
+// Codebook weights packed with the two-term operand (the record's split flag) issue a
+// second MFMA per k-step on the residual operand, so the product carries about 16
+// significant bits of each level instead of 8.
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "ql_common.hpp"
 #include "ql_decode.hpp"
 
 namespace ql {
 
-template <int FMT, bool ZP, int GS, int NT, int WK, int PF>
+template <int FMT, bool ZP, int GS, int NT, int WK, int PF, bool SW>
 __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int CH = chunk_k(FMT);
     constexpr int STEPS = CH / 32;
@@ -35,9 +48,14 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int S_OFF = NT * TILE_BYTES;
     constexpr int Z_OFF = S_OFF + 256 * NSS;
     constexpr int X_OFF = Z_OFF + 256 * NSZ;
-    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT);
-    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF);
-    static_assert(X_OFF + XB::BYTES == STAGE && S >= 1 && S <= 8, "stage layout");
+    constexpr int G_OFF = X_OFF + XB::BYTES;         // gate rows (SW)
+    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT, SW);
+    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF, SW);
+    static_assert(G_OFF + (SW ? 1024 : 0) == STAGE && S >= 1 && S <= 8, "stage layout");
+    // fused SwiGLU: the batch's rows fit the first activation load; each lane forms HE
+    // consecutive h values of one row
+    constexpr int HE = SWIGLU_FUSE_MAX_M * CH / 64;
+    static_assert(!SW || (SWIGLU_FUSE_MAX_M <= XB::RPI && (HE == 2 || HE == 4)), "fused SwiGLU rows");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // [WK][S][STAGE]
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -73,8 +91,14 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     const uint32_t s_shift = 16u * (c & 1);                       // this column's fp16/bf16 scale
     const uint32_t z_shift = 8u * ((c >> 1) & 3) + 4u * (c & 1);  // and its 4-bit zero-point
 
-    CbLut lut = {0u, 0u, 0u, 0u};
-    if (FMT == FMT_CB4) lut = reinterpret_cast<const CbRecord *>(a.aux)->lut;
+    CbLut lut = {0u, 0u, 0u, 0u}, lut2 = {0u, 0u, 0u, 0u};
+    uint32_t split = 0;
+    if (FMT == FMT_CB4) {
+        const CbRecord *cr = reinterpret_cast<const CbRecord *>(a.aux);
+        lut = cr->lut;
+        lut2 = cr->lut_lo;
+        split = uint32_t(__builtin_amdgcn_readfirstlane(int(cr->split)));
+    }
 
     // ---- per-lane parts of the loads ----
     // activation loads actually issued: those holding a row below M (wave-uniform)
@@ -158,10 +182,16 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                 const int k = kc * CH + xk[j];
                 const uint32_t past_k = uint32_t(~(int32_t(k - a.K) >> 31)) & 0x80000000u;   // k >= K
                 ld128_lds(xr, (xrow[j] + uint32_t(k) * 2u) | past_k, base + X_OFF + j * 1024);
+                // the gate half of the raw [up | gate] rows, same slots
+                if (SW) ld128_lds(xr, (xrow[j] + uint32_t(a.K + k) * 2u) | past_k, base + G_OFF);
             }
         }
     };
-    const int per_chunk = NT + NSS + NSZ + nia;   // vector-memory loads issued per chunk
+    // vector-memory loads issued per chunk
+    const int per_chunk = NT + NSS + NSZ + nia * (SW ? 2 : 1);
+    // fused SwiGLU: this lane's HE values -- row hr, inputs hk .. hk+HE-1 of the chunk
+    const int hr = (lane * HE) / CH, hk = (lane * HE) % CH;
+    const uint32_t h_off = uint32_t(XB::slot(hr, hk / 8) + (hk % 8) * 2);
 
     f32x4 acc[NT], tmp[NT], xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -172,12 +202,31 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     const u32x4 ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const bf16x8 ones = as_bf16x8(ones_u);
 
-    auto compute = [&](int i, int slot) {
+    auto compute = [&](int i, int slot, auto spl) {
+        constexpr bool SPLIT = decltype(spl)::value;
         const int kc = kc0 + i;
         // chunk i has landed once only the chunks issued after it are outstanding
         wait_vmcnt_rt(per_chunk * min(S - 1, nck - 1 - i));
         compiler_fence();
         const uint8_t *base = ring + slot * STAGE;
+        if constexpr (SW) {
+            // h = bf16(up * silu(gate)) over the batch's rows of this chunk, in place of up
+            // (LDS accesses of one wavefront complete in order: the fragment reads below
+            // see these writes)
+            uint8_t *hx = ring + slot * STAGE + X_OFF + h_off;
+            const uint8_t *gx = ring + slot * STAGE + G_OFF + h_off;
+            if constexpr (HE == 2) {
+                *reinterpret_cast<uint32_t *>(hx) =
+                    swiglu_pair(*reinterpret_cast<const uint32_t *>(hx), *reinterpret_cast<const uint32_t *>(gx));
+            } else {
+                const u32x2 up = *reinterpret_cast<const u32x2 *>(hx);
+                const u32x2 gt = *reinterpret_cast<const u32x2 *>(gx);
+                u32x2 h;
+                h.x = swiglu_pair(up.x, gt.x);
+                h.y = swiglu_pair(up.y, gt.y);
+                *reinterpret_cast<u32x2 *>(hx) = h;
+            }
+        }
         u32x4 wq[NT];
         uint32_t sq[NT][SPC], zq[NT][SPC];
 #pragma unroll
@@ -202,7 +251,13 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                 if (FMT == FMT_INT4) bw = dec_int4(wq[j][t]);
                 else if (FMT == FMT_INT8) bw = dec_int8<false>(wq[j][2 * t], wq[j][2 * t + 1]);
                 else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][t], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
-                else bw = dec_cb4(wq[j][t], lut);
+                else {
+                    bw = dec_cb4(wq[j][t], lut);
+                    if constexpr (SPLIT) {
+                        // the residual term first, then the leading term
+                        acc[j] = mfma16x16x32(af, as_bf16x8(dec_cb4(wq[j][t], lut2)), acc[j]);
+                    }
+                }
                 if (INTF) tmp[j] = mfma16x16x32(af, as_bf16x8(bw), tmp[j]);
                 else acc[j] = mfma16x16x32(af, as_bf16x8(bw), acc[j]);
             }
@@ -241,20 +296,24 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < S; ++u)
         if (u < nck) issue(u, u);
-    for (int i0 = 0; i0 < nck; i0 += S) {
+    auto main_loop = [&](auto spl) {
+        for (int i0 = 0; i0 < nck; i0 += S) {
 #pragma unroll
-        for (int u = 0; u < S; ++u) {
-            const int i = i0 + u;
-            if (i < nck) {
-                compute(i, u);
-                if (i + S < nck) {
-                    // the slot is refilled: this wavefront's reads of it must be complete
-                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    issue(i + S, u);
+            for (int u = 0; u < S; ++u) {
+                const int i = i0 + u;
+                if (i < nck) {
+                    compute(i, u, spl);
+                    if (i + S < nck) {
+                        // the slot is refilled: this wavefront's accesses of it must be complete
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        issue(i + S, u);
+                    }
                 }
             }
         }
-    }
+    };
+    if (FMT == FMT_CB4 && split) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
 
     // ---- wavefront reduction in LDS (fixed order), then the epilogue ----
     __syncthreads();                      // every ring is drained: reuse the LDS

@@ -25,6 +25,7 @@ hipError_t launch_lora_merge8(const Layout &L, void *pw, void *ps, const void *m
 
 // One translation unit per format family keeps the template instantiations apart.
 hipError_t launch_gemm_int4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_int4_zp(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_int8(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_cb4(const Layout &L, const Plan &p, const GemmArgs &a, hipStream_t st);

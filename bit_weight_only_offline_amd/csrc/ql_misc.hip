@@ -1,10 +1,9 @@
 // Small kernels around the linear: the split-K reduce of the tile schedules and the
-// SwiGLU prologue of the decode schedules.
+// SwiGLU prologue that materialises h when the linear kernel does not form it itself.
 #include <hip/hip_runtime.h>
 
 #include "ql_common.hpp"
 #include "ql_decode.hpp"
-#include "ql_gemm.hpp"
 #include "ql_launch.hpp"
 
 namespace ql {

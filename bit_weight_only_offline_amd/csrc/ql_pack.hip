@@ -218,14 +218,29 @@ __global__ void __launch_bounds__(256) unpack_cb_scales_kernel(const uint16_t *_
 }
 
 // ---- CB4 record: choose alpha in [1, 2) (steps of 2^-12) minimising the summed squared
-// relative bf16 rounding error of alpha * c[8 + m], then store the LUT planes.
+// relative bf16 rounding error of alpha * c[8 + m], then store the LUT planes of the
+// leading term hi_m = bf16(alpha c[8 + m]) and of the residual lo_m = bf16(alpha c[8 + m]
+// - hi_m), and choose between the one-term and the two-term operand.
+//
+// The one-term operand rounds each level once to bf16 (about 1e-3 relative error after
+// alpha).  That error is relative to each row's own output, so a row whose norm stands
+// far above the others carries it into outputs that dominate the whole matrix, and the
+// error measured against the rms of all outputs grows with max(norm) / rms(norm) (about
+// 1.4e-3 at a ratio of one, measured on the 3072 x 3072 workload).  Above a ratio of
+// CB_SPLIT_RATIO the kernels take the two-term operand (two MFMAs per fragment, about
+// 16 bits per level).  The ratio is a property of the norms alone, decided once here.
 struct Centroids { float c[16]; };
+
+constexpr float CB_SPLIT_RATIO = 3.0f;
 
 __device__ inline float bf16_rne(float v) { return __uint_as_float(uint32_t(__builtin_bit_cast(uint16_t, (__bf16)v)) << 16); }
 
-__global__ void __launch_bounds__(256) cb_record_kernel(Centroids cs, CbRecord *__restrict__ rec) {
+__global__ void __launch_bounds__(256) cb_record_kernel(Centroids cs, const uint16_t *__restrict__ norms, int N,
+                                                        CbRecord *__restrict__ rec) {
     __shared__ float best_cost[256];
     __shared__ int best_idx[256];
+    __shared__ double sq[256];
+    __shared__ float mx[256];
     const int t = threadIdx.x;
     float bc = INFINITY;
     int bi = 0;
@@ -242,6 +257,16 @@ __global__ void __launch_bounds__(256) cb_record_kernel(Centroids cs, CbRecord *
     }
     best_cost[t] = bc;
     best_idx[t] = bi;
+    // norm statistics: max and the float64 sum of squares, thread-strided then a tree
+    double s2 = 0.0;
+    float m2 = 0.0f;
+    for (int n = t; n < N; n += 256) {
+        const float v = fabsf(bf16_bits_to_f32(norms[n]));
+        s2 += double(v) * double(v);
+        m2 = fmaxf(m2, v);
+    }
+    sq[t] = s2;
+    mx[t] = m2;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
         if (t < s) {
@@ -251,6 +276,8 @@ __global__ void __launch_bounds__(256) cb_record_kernel(Centroids cs, CbRecord *
                 best_cost[t] = oc;
                 best_idx[t] = oi;
             }
+            sq[t] += sq[t + s];
+            mx[t] = fmaxf(mx[t], mx[t + s]);
         }
         __syncthreads();
     }
@@ -258,19 +285,31 @@ __global__ void __launch_bounds__(256) cb_record_kernel(Centroids cs, CbRecord *
         const float a = 1.0f + float(best_idx[0]) * (1.0f / 4096.0f);
         CbRecord r;
         for (int j = 0; j < 16; ++j) r.centroids[j] = cs.c[j];
-        uint32_t lo[2] = {0, 0}, hi[2] = {0, 0};
+        uint32_t lo[2] = {0, 0}, hi[2] = {0, 0}, rlo[2] = {0, 0}, rhi[2] = {0, 0};
         for (int m = 0; m < 8; ++m) {
-            const uint32_t b = __float_as_uint(bf16_rne(a * cs.c[8 + m])) >> 16;
+            const float p = a * cs.c[8 + m];
+            const float h = bf16_rne(p);
+            const uint32_t b = __float_as_uint(h) >> 16;
+            const uint32_t rb = __float_as_uint(bf16_rne(p - h)) >> 16;   // p - h is exact in float32
             lo[m >> 2] |= (b & 0xFFu) << (8 * (m & 3));
             hi[m >> 2] |= (b >> 8) << (8 * (m & 3));
+            rlo[m >> 2] |= (rb & 0xFFu) << (8 * (m & 3));
+            rhi[m >> 2] |= (rb >> 8) << (8 * (m & 3));
         }
         r.lut.lo0 = lo[0];
         r.lut.lo1 = lo[1];
         r.lut.hi0 = hi[0];
         r.lut.hi1 = hi[1];
+        r.lut_lo.lo0 = rlo[0];
+        r.lut_lo.lo1 = rlo[1];
+        r.lut_lo.hi0 = rhi[0];
+        r.lut_lo.hi1 = rhi[1];
         r.inv_alpha = 1.0f / a;
         r.alpha = a;
-        for (int j = 0; j < 10; ++j) r.pad[j] = 0;
+        // max > ratio * rms, i.e. max^2 * N > ratio^2 * sum of squares
+        const double rms2n = sq[0];
+        r.split = (double(mx[0]) * double(mx[0]) * double(N) > double(CB_SPLIT_RATIO) * CB_SPLIT_RATIO * rms2n) ? 1u : 0u;
+        for (int j = 0; j < 5; ++j) r.pad[j] = 0;
         *rec = r;
     }
 }
@@ -310,7 +349,16 @@ __global__ void __launch_bounds__(256) dequant_tile_kernel(const u32x4 *__restri
         op = dec_cb4(rec[t], cr->lut);
     }
     const uint32_t bits = (op[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-    const float v = bf16_bits_to_f32(bits);
+    float v = bf16_bits_to_f32(bits);
+    if (FMT == FMT_CB4) {
+        // with the two-term operand the image is hi + lo, exact in float32 (lo is below
+        // half an ulp of hi's 8 bits and carries 8 bits itself)
+        const CbRecord *cr = reinterpret_cast<const CbRecord *>(aux);
+        if (cr->split) {
+            const u32x4 op2 = dec_cb4(rec[t], cr->lut_lo);
+            v += bf16_bits_to_f32((op2[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
+    }
     float d;
     if (mode == 1) {
         d = v;
@@ -399,7 +447,8 @@ hipError_t launch_pack(const Layout &L, const void *codes, const void *scales, c
                            sqrt_k);
         Centroids cs;
         for (int j = 0; j < 16; ++j) cs.c[j] = ((const float *)aux_in)[j];
-        hipLaunchKernelGGL(cb_record_kernel, dim3(1), dim3(256), 0, st, cs, (CbRecord *)paux);
+        hipLaunchKernelGGL(cb_record_kernel, dim3(1), dim3(256), 0, st, cs, (const uint16_t *)scales, N,
+                           (CbRecord *)paux);
     }
     return hipGetLastError();
 }

@@ -22,7 +22,8 @@
  *             (AutoRound Kernel, "1. Linear", "Example": qweight, scale and zp per group;
  *              "Supported Data Types": sym / asym)
  *   QL_MXFP4  codes  uint8 [N, K/2]  E2M1 codes (sign, 2 exponent bits bias 1, 1 mantissa)
- *             scales uint8 [N, K/32] E8M0 codes c -> 2^(c-127); G must be 32
+ *             scales uint8 [N, K/32] E8M0 codes c -> 2^(c-127), code 255 = NaN (its
+ *                                    block decodes to NaN); G must be 32
  *             (Petit package description, "Features": MXFP4 weights)
  *   QL_INT8   codes  int8  [N, K]    q in [-128, 127]
  *             scales bf16  [N, K/G]  G in {32, 64, 128, 256}; 256 is ConvRot's group
@@ -106,7 +107,12 @@ ql_status qlinear_packed_bytes(ql_format f, int64_t N, int64_t K, int group, int
  *   packed_w, packed_s, packed_aux   outputs sized by qlinear_packed_bytes()
  *           (packed_aux may be NULL when aux_bytes is 0)
  * CB4 also chooses a per-codebook multiplier alpha in [1, 2) that minimises the bf16
- * rounding error of alpha * c[j] and records it in packed_aux.
+ * rounding error of alpha * c[j] and records it in packed_aux, together with the
+ * matrix-core operand the kernels will use: one bf16 term per level (about 1e-3 relative
+ * error, one MFMA per fragment), or two terms hi + lo (about 16 bits, two MFMAs) when the
+ * largest row norm exceeds 3 x their rms -- the single term's error is relative to each
+ * row's own output, so a dominant row would carry it into the outputs that set the
+ * output's rms.  The choice is taken on the device from the norms, once, here.
  * Errors: QL_E_UNSUPPORTED for a codebook that is not symmetric or not finite.
  */
 ql_status qlinear_pack(ql_format f, int64_t N, int64_t K, int group,
@@ -180,7 +186,9 @@ ql_status qlinear_int8_addmm(int64_t N, int64_t K, int group, void *packed_w, vo
                              int stochastic, uint64_t seed, void *stream);
 
 /*
- * Inverse of qlinear_pack(): device layout -> canonical arrays, bit-exact.
+ * Inverse of qlinear_pack(): device layout -> canonical arrays, bit-exact (AutoRound
+ * Kernel package description, "1. Linear": unpack_weight recovers the weight from the
+ * packed blob, for verification).
  *   codes, scales   canonical outputs
  *   aux_out         INT4 with zeros: zeros [N, K/G]; CB4: float32 centroids [16]
  *                   (device); otherwise NULL
@@ -192,11 +200,14 @@ ql_status qlinear_unpack(ql_format f, int64_t N, int64_t K, int group, int has_z
 
 /*
  * Debug dump of a dequantised weight tile, decoded by the same register-level code
- * the GEMM kernels use.
+ * the GEMM kernels use (AutoRound Kernel package description, "1. Linear":
+ * unpack_weight dequantises the packed blob to a dense weight, for verification; here
+ * a tile of it at a time).
  *   n0, k0, tn, tk  tile origin and extent (0 <= n0, n0+tn <= N, same for k)
  *   mode 0          out = D(Wq)[n0.., k0..] in float32, exactly as the format defines it
  *   mode 1          out = the bf16 operand the matrix cores receive, widened to float32
- *                   (before group, zero-point and codebook row scaling)
+ *                   (before group, zero-point and codebook row scaling; a two-term
+ *                   codebook operand as the float32 sum hi + lo, which is exact)
  *   out             float32 [tn, tk] row-major
  */
 ql_status qlinear_dequant_tile(ql_format f, int64_t N, int64_t K, int group, int has_zeros,
@@ -209,9 +220,10 @@ ql_status qlinear_dequant_tile(ql_format f, int64_t N, int64_t K, int group, int
  * dimension over workgroups is scheduled.  Host-only (the schedule is a pure function
  * of the shape, fixed for the 256 compute units of gfx950).
  *
- * The workspace holds float32 split-K partial sums (tile schedules) or the bf16 SwiGLU
- * input h (decode schedules with act = SWIGLU).  Its contents on entry do not matter
- * and are overwritten; calls that run at the same time must not share one.
+ * The workspace holds float32 split-K partial sums (tile schedules) and the bf16 SwiGLU
+ * input h when a prologue materialises it (act = SWIGLU, except decode schedules with
+ * M <= 2, whose kernel forms h itself).  Its contents on entry do not matter and are
+ * overwritten; calls that run at the same time must not share one.
  */
 ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, int group,
                                   ql_act act, size_t *bytes);
@@ -230,7 +242,9 @@ ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, 
  * Schedules: for M <= 16 one workgroup per block of output columns streams the whole
  * input dimension, split over its wavefronts and reduced in LDS; larger M uses tiles of
  * 32 to 128 rows with activations staged through LDS, split over workgroups when the
- * column blocks alone do not fill the device.  Both accumulate in float32 and add
+ * column blocks alone do not fill the device.  The SwiGLU input is formed by a one-pass
+ * prologue, or inside the decode kernel for M <= 2; both give the same h, so the fused
+ * and the materialised paths give the same linear (piper-kernels, "ConvRot INT8").  Both accumulate in float32 and add
  * partial sums in a fixed order, so repeated calls give bit-identical results.
  */
 ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K,
@@ -249,9 +263,8 @@ ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K,
  *           schedules split the input dimension over the wavefronts of one workgroup
  *           and take splits 0 or 1; they serve M <= 16 only (QL_E_UNSUPPORTED
  *           otherwise)
- * A schedule whose launch grid exceeds the device's limits (more than 65535 splits, or
- * more than 65535 row blocks for the tiles that take the row blocks as the grid's
- * second dimension) is refused with QL_E_UNSUPPORTED before any launch.
+ * A schedule whose launch grid exceeds the device's limits (more than 65535 splits) is
+ * refused with QL_E_UNSUPPORTED before any launch.
  */
 typedef struct ql_schedule {
     int32_t tile;
@@ -259,8 +272,8 @@ typedef struct ql_schedule {
 } ql_schedule;
 
 /* Number of compiled schedules, and for each the rows x columns of output of one
- * workgroup and the activation block it stages per barrier (0 for decode schedules,
- * which read activations straight into registers). */
+ * workgroup and the inputs it stages per barrier (0 for decode schedules, whose
+ * wavefronts stream their own chunks without a workgroup barrier). */
 int qlinear_num_tiles(void);
 ql_status qlinear_tile_shape(int tile, int *rows, int *cols, int *kblock);
 

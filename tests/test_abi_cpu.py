@@ -246,15 +246,6 @@ def test_launch_grid_limits(L):
     assert L.qlinear_workspace_bytes_ex(CB4, 1, 16, K, 0, 0, ctypes.byref(over), ctypes.byref(b)) == QL_E_UNSUPPORTED
     assert L.qlinear_forward_ex(FAKE, 1, 16, K, FAKE, FAKE, FAKE, CB4, 0, 0, None, 0, FAKE, 0, FAKE, 1 << 40,
                                 ctypes.byref(over), None) == QL_E_UNSUPPORTED
-    # tiles whose row blocks are the grid's second dimension: 65536 row blocks are refused
-    kind1 = [(t, rows) for t, rows, cols, kb in kinds if kb > 128]
-    if kind1:
-        t, rows = kind1[0]
-        s1 = Sched(t, 1)
-        assert L.qlinear_workspace_bytes_ex(INT4, 65535 * rows, 16, 128, 128, 0, ctypes.byref(s1),
-                                            ctypes.byref(b)) == QL_OK
-        assert L.qlinear_workspace_bytes_ex(INT4, 65536 * rows, 16, 128, 128, 0, ctypes.byref(s1),
-                                            ctypes.byref(b)) == QL_E_UNSUPPORTED
     # grouped: ceil(T/16) + E decode slots past 65535 are served by the 32-row ring tile,
     # whose slot map (ceil(T/32) + E pairs of int32) sizes the workspace
     T = E = 70000

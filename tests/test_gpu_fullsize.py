@@ -7,7 +7,9 @@ outputs one by one (rows x columns including the first and last of each), which 
 checked against the float32 output of the kernel (G2 on the sample, with the rms of
 the sampled reference).  Properties that hold at any size are checked on the whole
 output: the bf16 output is the RNE rounding of the float32 output (G3), two runs are
-bit-identical, and no output is NaN or infinite.
+bit-identical, and no output is NaN or infinite.  The literal bf16 gate (G4) is printed
+for each case next to the same figure for the correctly rounded bf16 of the exact
+answer, which no bf16 output can beat.
 """
 import zlib
 
@@ -89,5 +91,53 @@ def test_full_size_sampled_parity(name, M):
     got = y32.cpu().numpy()[rr.ravel(), cc.ravel()].astype(np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2)))
     err = float(np.max(np.abs(got - ref))) / rms
-    print(f"  sampled {len(ref)} outputs: max|dY|/rms = {err:.3e}", flush=True)
+    # G4: the bf16 output itself, and the correctly rounded bf16 of the exact answer
+    got16 = y16.float().cpu().numpy()[rr.ravel(), cc.ravel()].astype(np.float64)
+    g4 = float(np.max(np.abs(got16 - ref))) / rms
+    g4_exact = float(np.max(np.abs(O.bf16_from_f64(ref).astype(np.float64) - ref))) / rms
+    print(f"  sampled {len(ref)} outputs: G2 max|dY|/rms = {err:.3e}; G4 bf16 output {g4:.3e}, "
+          f"correctly rounded exact answer {g4_exact:.3e}", flush=True)
     assert err <= TOL
+
+
+def _record_split(pw) -> int:
+    """The codebook record's operand choice (bytes 104..107): 1 = two-term operand."""
+    return int(pw.aux.cpu().numpy()[104:108].view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("M", [256, 2048])
+def test_codebook_dominant_rows_full_size(M):
+    """The 3072 x 3072 codebook workload with four rows scaled by 100: those rows'
+    outputs dominate rms(Y), so the single bf16 rounding of each level would show up in
+    the gate; the packer sees the spread of the row norms and the kernels take the
+    two-term operand.  The whole output is checked against the oracle (G2, G3)."""
+    import bit_weight_only_offline_amd as Q
+    wl = S.WORKLOADS["cb4_prefill"]
+    N, K = wl["N"], wl["K"]
+    w = S.weights(wl)
+    rows = np.array([5, 700, 1901, 3070])
+    w[rows] *= np.float32(100.0)
+    canon = quantize("cb4", w, 0)
+    codes, scales, aux = to_device("cb4", canon)
+    pw = Q.pack("cb4", N, K, 0, codes, scales, aux)
+    assert _record_split(pw) == 1
+    x_all = S.activations(wl, M)
+    b = S.bias(wl)
+    print(f"codebook dominant rows M={M} schedule={Q.default_schedule('cb4', M, N, K, 0)}", flush=True)
+    x = torch.from_numpy(np.ascontiguousarray(x_all)).cuda().to(torch.bfloat16)
+    bias = torch.from_numpy(b).cuda().to(torch.bfloat16)
+    y32 = Q.linear(x, pw, bias=bias, out_dtype=torch.float32)
+    y16 = Q.linear(x, pw, bias=bias)
+    torch.cuda.synchronize()
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16)), "G3"
+    ref = O.forward("cb4", x_all, canon, K, b)
+    err = float(np.max(np.abs(y32.cpu().numpy().astype(np.float64) - ref))) / float(np.sqrt(np.mean(ref ** 2)))
+    print(f"  whole output: G2 max|dY|/rms = {err:.3e}", flush=True)
+    assert err <= TOL
+
+
+def test_codebook_workload_keeps_one_term_operand():
+    """The workload's own weights (row norms within a few percent of each other) keep the
+    single bf16 operand: one MFMA per fragment."""
+    _, _, pw, _, _ = _prepared("cb4_prefill")
+    assert _record_split(pw) == 0

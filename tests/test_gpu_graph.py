@@ -63,11 +63,13 @@ def _same(a, b):
 
 
 # (format, group, symmetric, M, N, K, act, schedule): the decode kernel, the ring tiles with
-# and without split-K (then the reduce kernel), the fused and materialised SwiGLU inputs
+# and without split-K (then the reduce kernel), the SwiGLU input formed by the decode
+# kernel itself (one row) and materialised by the prologue
 LINEAR = [
     ("int4", 128, False, 16, 512, 4096, None, None),
     ("int4", 64, True, 200, 320, 1024, None, None),
     ("mxfp4", 32, True, 64, 512, 2048, None, (12, 4)),
+    ("int8", 256, True, 1, 256, 2048, "swiglu", None),
     ("int8", 256, True, 16, 256, 2048, "swiglu", None),
     ("int8", 256, True, 130, 256, 1024, "swiglu", None),
     ("cb4", 0, True, 300, 384, 768, None, None),

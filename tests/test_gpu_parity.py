@@ -140,21 +140,53 @@ def test_dequant_tile_operand_mode_is_exact_bf16_image():
         p = (np.float32(a) * c[8:]).astype(np.float32)
         return float(np.sum(((O.bf16_round(p) - p) / np.float32(a)).astype(np.float64) ** 2))
     assert cost(alpha) <= cost(1.0)
+    assert int(rec[104:108].view(np.uint32)[0]) == 0          # one-term operand: norms alike
+
+
+def test_codebook_two_term_operand_image():
+    """A weight with one row 50x the others takes the two-term codebook operand: mode 1
+    returns hi + lo with hi = bf16(alpha*c) and lo = bf16(alpha*c - hi) (float32 values),
+    and mode 0 stays the oracle's D(W) bit for bit."""
+    Q = _lib()
+    N, K = 40, 256
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[7] *= np.float32(50.0)
+    case = ("cb4", "cb4", 0, True, N, K)
+    pw, canon, _ = _packed(case, w=w)
+    rec = pw.aux.cpu().numpy()
+    assert int(rec[104:108].view(np.uint32)[0]) == 1
+    alpha = rec[84:88].view(np.float32)[0]
+    c = canon["centroids"]
+    p = (np.float32(alpha) * c[8:]).astype(np.float32)
+    hi = O.bf16_round(p)
+    lo = O.bf16_round((p - hi).astype(np.float32))
+    mag = (hi + lo).astype(np.float32)
+    idx = O.unpack_nibbles(canon["codes"]).astype(np.int64)
+    expect = np.where(idx >= 8, mag[np.clip(idx - 8, 0, 7)], -mag[np.clip(7 - idx, 0, 7)])
+    op = Q.dequant_tile(pw, mode=1).cpu().numpy()
+    assert np.array_equal(op, expect.astype(np.float32))
+    ref = O.dequant("cb4", canon, K)
+    assert np.array_equal(Q.dequant_tile(pw).cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
 def test_mxfp4_extreme_scales_dequant_exact():
-    """E8M0 codes at both ends of the range decode exactly (including 2^-127)."""
+    """E8M0 codes at both ends of the range decode exactly (including 2^-127 and the
+    largest finite scale 2^127); code 255 is NaN (OCP MX) and gives NaN for every element,
+    zero included, as in the oracle."""
     Q = _lib()
     N, K = 16, 256
     rng = np.random.default_rng(3)
     q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
-    e = np.array([0, 1, 2, 5, 100, 127, 200, 250], dtype=np.uint8)[rng.integers(0, 8, size=(N, K // 32))]
+    e = np.array([0, 1, 2, 5, 100, 127, 200, 250, 254, 255], dtype=np.uint8)[rng.integers(0, 10, size=(N, K // 32))]
     canon = dict(codes=O.pack_nibbles(q), scales=e, group=32)
     codes, scales, _ = to_device("mxfp4", canon)
     pw = Q.pack("mxfp4", N, K, 32, codes, scales)
     got = Q.dequant_tile(pw).cpu().numpy()
     ref = O.dequant("mxfp4", canon, K)
-    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    nan = np.isnan(ref)
+    assert nan.any() and np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
 
 
 FWD_CASES = [c for c in CASES]
@@ -200,10 +232,10 @@ def _device_h(Q, raw, K):
 
 
 @pytest.mark.parametrize("fmt,G", [("int8", 256), ("int4", 128), ("mxfp4", 32), ("cb4", 0)])
-@pytest.mark.parametrize("M,N", [(1, 40), (16, 40), (70, 40), (40, 300), (130, 600)])
+@pytest.mark.parametrize("M,N", [(1, 40), (2, 300), (3, 40), (16, 40), (70, 40), (40, 300), (130, 600)])
 def test_swiglu_fused_equals_materialised(fmt, G, M, N):
-    """The SwiGLU input stage (fused into the tile kernel's activation staging for narrow
-    outputs, a one-pass prologue otherwise) computes the same linear as materialising
+    """The SwiGLU input stage (formed by the decode kernel itself for batches of one or
+    two rows, a one-pass prologue otherwise) computes the same linear as materialising
     h = bf16(up * silu(gate)) first (piper-kernels, "ConvRot INT8"): bit-identical to the
     linear of the device's own h, and within the tolerance of the oracle."""
     Q = _lib()
@@ -221,14 +253,8 @@ def test_swiglu_fused_equals_materialised(fmt, G, M, N):
     torch.cuda.synchronize()
     assert rel_err(y_fused.cpu().numpy(), yref) <= TOL
     assert torch.equal(y_fused, y_dev_h)
-    if M > 16:
-        # the tile kernel forms h while staging the activations when few column blocks
-        # would recompute it: same result as that kernel on the materialised h
-        y_k1 = Q.linear(bf16_tensor(raw), pw, bf16_tensor(b), act="swiglu", out_dtype=torch.float32, schedule=(4, 0))
-        y_k1_h = Q.linear(hd, pw, bf16_tensor(b), out_dtype=torch.float32, schedule=(4, 0))
-        torch.cuda.synchronize()
-        assert torch.equal(y_k1, y_k1_h)
-        assert rel_err(y_k1.cpu().numpy(), yref) <= TOL
+    # fused (no workspace for h) exactly for the decode kernel's one- and two-row batches
+    assert (Q.workspace_bytes(fmt, M, N, K, G, "swiglu") == 0) == (M <= 2)
     # the device's h is within one bf16 step of the oracle's (float32 exp and reciprocal
     # against float64), and such differences are rare
     h_or = O.swiglu_bf16(raw)

@@ -24,7 +24,7 @@ def _lib():
     return Q
 
 
-def _weights(fmt, N, K, G, seed, huge=True):
+def _weights(fmt, N, K, G, seed):
     """Gaussian weights with planted special groups (each a whole group of one row)."""
     rng = np.random.default_rng(seed)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
@@ -35,8 +35,7 @@ def _weights(fmt, N, K, G, seed, huge=True):
     # all-zero group, tiny group (amax in the float32 subnormal range), huge-ish group
     specials.append(np.zeros(g, np.float32))
     specials.append((rng.standard_normal(g) * 1e-41).astype(np.float32))
-    if huge:
-        specials.append((rng.standard_normal(g) * 3.0).astype(np.float32))
+    specials.append((rng.standard_normal(g) * 3.0).astype(np.float32))
     if fmt == "int4":
         s = np.float32(np.float16(0.01))                       # an fp16 step
         q = rng.integers(-7, 8, g).astype(np.float32)
@@ -111,17 +110,18 @@ def test_quantize_matches_oracle_bit_exact(fmt, G, sym, N, K):
 def test_quantize_then_pack_then_forward(fmt, G, sym):
     """Device quantiser -> pack -> linear, against the oracle's quantise -> linear.
 
-    The codebook's matrix-core operand is the bf16 rounding of alpha * level (relative
-    error about 1e-3 per level), so its error scales with each row's own output; a
-    planted row 150x larger than the rest would dominate rms(Y) and push the global
-    max/rms ratio to about 1e-2.  That row is left out here for the codebook only (the
-    other formats feed exact operands and keep it)."""
+    The planted row 150x larger than the rest dominates rms(Y).  For the codebook the
+    single bf16 rounding of each level (relative error about 1e-3) would then reach the
+    1e-2 gate; the packer sees the spread of the row norms and selects the two-term
+    operand, which the record's split flag shows."""
     Q = _lib()
     N, K, M = 96, 1024, 24
-    w = _weights(fmt, N, K, G, seed=5, huge=(fmt != "cb4"))
+    w = _weights(fmt, N, K, G, seed=5)
     canon = _oracle(fmt, w, G, sym)
     codes, scales, aux = _device(fmt, w, G, sym)
     pw = Q.pack(fmt, N, K, G, codes, scales, aux)
+    if fmt == "cb4":
+        assert int(pw.aux.cpu().numpy()[104:108].view(np.uint32)[0]) == 1
     x = S.to_bf16_values(np.random.default_rng(3).standard_normal((M, K)).astype(np.float32))
     y = Q.linear(torch.from_numpy(x).cuda().to(torch.bfloat16), pw, out_dtype=torch.float32)
     torch.cuda.synchronize()
