@@ -3,30 +3,42 @@
 One step = one forward of the INT4 decode workload with zero-points (group 128, fp16
 scales, 4-bit zeros): X bf16 [16, 4096] times a packed 4096 x 4096 weight, bf16 out.
 The metric is effective HBM bandwidth: algorithmic bytes (packed weight + scales +
-zero-points + X + Y) per step over the step time.  Each step reads a different copy
-of the packed weight from a pool larger than twice the 256 MB Infinity Cache, so the
-weights come from HBM.  Steps run back to back inside a HIP graph (the launch-bound
-inner loop), timed with HIP events on the stream the kernels run on.
+zero-points + X + Y) per step over the step time.  Steps run back to back inside a
+HIP graph (the launch-bound inner loop), each on the next copy of the packed weight
+from a pool larger than four times the 256 MB Infinity Cache, timed with HIP events on
+the stream the kernels run on.  Before every timed replay a 1 GiB buffer is read, so
+the timed forwards find none of their weights in the caches, whatever the step count.
 
-Also reported, on the same line:
-  prefill  the 4-bit codebook workload at M = 2048 (3072 x 3072): TFLOP/s and the
-           fraction of the dense bf16 matrix-core peak
-  roofline the decode kernel (the only kernel of the step) against the HBM peak
-           (8 TB/s), with the HBM traffic its FETCH_SIZE / WRITE_SIZE counters read
-           (calibrated on a plain copy), when recorded for the current kernel source
-  cpu_baseline  the CPU oracle (dequantise, then a float64 product) on a bounded
-           sample of the same workload, on the host cores
-  sweep    (--sweep) the decode workload at M = 1, 4, 8, the other workloads, the grouped
-           (mixture-of-experts) linear, the on-device quantiser (float32 weights in,
-           canonical codes out), the in-place INT8 low-rank merge and the INT8-compute
-           (W4A8 / W8A8) linear
+Also reported, on the same line (each leg timed the same way, with at least one forward
+per pool copy in the graph, the clocks settled by 0.25 s of untimed replays, the median
+of three timed replays):
+  decode   every decode-sized workload: INT4 4096 x 4096 at M = 1, 4, 8, 16; MXFP4
+           28672 x 4096 (gate/up) and 4096 x 14336 (down) at M = 1, 16; INT8 group
+           256 with the fused SwiGLU input, 8192 x 28672, at M = 1, 16: time, effective
+           GB/s and the fraction of the 8 TB/s HBM peak, with the HBM traffic the
+           kernels' FETCH_SIZE / WRITE_SIZE counters read (calibrated on a plain copy)
+           when recorded for the current kernel sources
+  prefill  the 4-bit codebook workload (3072 x 3072) at M = 2048 and 256: TFLOP/s and the
+           fraction of the 2.5 PFLOP/s dense bf16 matrix-core peak, with the matrix-core
+           busy fraction and the engine clock from the kernels' counters when recorded
+           for the current kernel sources
+  roofline the decode kernel of the step (its only kernel) against the HBM peak
+  cpu_baseline  the CPU oracle on the same INT4 workload on the host cores, in the two
+           reference styles of the OrbitQuant benchmark (dequantise then multiply on
+           every call; a weight dequantised once, the product only) and a float32 product
+  sweep    (--sweep) MXFP4 at M = 64, INT8 SwiGLU at M = 128, every weight format at the
+           codebook prefill's shape, torch's dense bf16 product there (context), the
+           grouped (mixture-of-experts) linear, the on-device quantiser, the in-place INT8
+           low-rank merge and the INT8-compute (W4A8 / W8A8) linear
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--sweep]
 Profiling helpers (used to write the summaries kept with the benchmark):
-  python bench.py --probe [decode|prefill]   copy calibration + 20 decode dispatches, or
-                                       20 prefill dispatches; no timing
-  python bench.py --summarize-trace D  per-kernel durations from a rocprofv3 CSV trace
-  python bench.py --summarize-pmc F W  traffic per dispatch from FETCH_SIZE / WRITE_SIZE runs
+  python bench.py --probe decode|prefill   counter-collection workloads, no timing
+  python bench.py --summarize-trace D      per-kernel durations from a rocprofv3 CSV trace
+  python bench.py --summarize-pmc F W      decode traffic per forward from FETCH_SIZE /
+                                           WRITE_SIZE runs of --probe decode
+  python bench.py --summarize-prefill P T  matrix-core busy and clock per prefill leg from
+                                           a counter run and a trace run of --probe prefill
 """
 from __future__ import annotations
 
@@ -36,6 +48,7 @@ import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -46,15 +59,36 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
-POOL_BYTES = 1 << 30           # > 2 x the 256 MB Infinity Cache
-AUX_WARM_S = 0.25              # untimed replays before each timed leg after the main step
+POOL_BYTES = 1 << 30           # > 4 x the 256 MB Infinity Cache
+FLUSH_BYTES = 1 << 30          # read before every timed replay
+AUX_WARM_S = 0.25              # untimed replays before each timed leg
 COPY_BYTES = 256 << 20         # calibration copy for the traffic counters
+SIMDS = 1024                   # 256 compute units x 4
+XCDS = 8
 
-# sources that define the decode kernel the roofline reports on; a recorded traffic
-# figure is used only while their hash is the one it was measured with
-KERNEL_SOURCES = ["ql_gemv.hpp", "ql_decode.hpp", "ql_common.hpp", "ql_gemm_dispatch.hpp", "ql_gemm_int4.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qgemv_int4_asym_decode_m16.txt")
-DECODE_KERNEL = "qgemv_kernel<0, true, 4"     # prefix of the INT4 zero-point g128 instantiation
+# decode legs of the default line: (label, workload, M); the step is the INT4 M = 16 leg
+DECODE_LEGS = [
+    ("int4_asym_g128_4096x4096/M1", "int4_asym_decode", 1),
+    ("int4_asym_g128_4096x4096/M4", "int4_asym_decode", 4),
+    ("int4_asym_g128_4096x4096/M8", "int4_asym_decode", 8),
+    ("int4_asym_g128_4096x4096/M16", "int4_asym_decode", 16),
+    ("mxfp4_up_28672x4096/M1", "mxfp4_up", 1),
+    ("mxfp4_up_28672x4096/M16", "mxfp4_up", 16),
+    ("mxfp4_down_4096x14336/M1", "mxfp4_down", 1),
+    ("mxfp4_down_4096x14336/M16", "mxfp4_down", 16),
+    ("int8_g256_swiglu_8192x28672/M1", "int8_swiglu", 1),
+    ("int8_g256_swiglu_8192x28672/M16", "int8_swiglu", 16),
+]
+MAIN_LEG = "int4_asym_g128_4096x4096/M16"
+PREFILL_LEGS = [
+    ("cb4_3072x3072/M2048", "cb4_prefill", 2048),
+    ("cb4_3072x3072/M256", "cb4_prefill", 256),
+]
+# kernels of a forward (names as the traces show them)
+FORWARD_KERNELS = ("qgemv_kernel", "qgemm_lds_kernel", "qmm_kernel", "qreduce_kernel", "swiglu_kernel")
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_legs.txt")
+PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_prefill_cb4.txt")
 
 
 def alg_bytes(fmt, M, N, K, G, zeros, swiglu=False, bias=False):
@@ -72,6 +106,11 @@ def alg_bytes(fmt, M, N, K, G, zeros, swiglu=False, bias=False):
     a = M * (2 * K if swiglu else K) * 2
     y = M * N * 2
     return w + s + a + y + (2 * N if bias else 0)
+
+
+def leg_bytes(wl, M):
+    return alg_bytes(wl["fmt"], M, wl["N"], wl["K"], wl["group"], not wl.get("symmetric", True),
+                     bool(wl.get("swiglu")), wl.get("bias_std") is not None)
 
 
 def _canonical(fmt, N, K, G, sym, seed):
@@ -112,28 +151,40 @@ def _pool(Q, fmt, N, K, G, sym, seed, pool_bytes):
     return pool
 
 
+def _leg_pool(Q, wl, seed, pool_bytes=POOL_BYTES):
+    return _pool(Q, wl["fmt"], wl["N"], wl["K"], wl["group"], wl.get("symmetric", True), seed, pool_bytes)
+
+
 def kernel_source_hash() -> str:
+    """sha256 over every kernel source of the library: a recorded counter figure is
+    used only while it matches."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bit_weight_only_offline_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    d = os.path.join(ROOT, "bit_weight_only_offline_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode())
+                h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per decode launch recorded in the counter summary, or None when the
-    summary is missing or was measured on another version of the kernel sources."""
+def recorded(path):
+    """{label: {key: value}} from a counter summary, or {} when it is missing or was
+    measured on other kernel sources.  Lines 'leg <label> <key>=<value> ...'."""
     try:
-        with open(TRAFFIC_FILE) as fh:
-            kv = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith(" "))
+        with open(path) as fh:
+            lines = fh.read().splitlines()
     except OSError:
-        return None
+        return {}
+    kv = dict(ln.split(":", 1) for ln in lines if ":" in ln and not ln.startswith(("#", " ", "leg ")))
     if kv.get("source_sha256", "").strip() != kernel_source_hash():
-        return None
-    try:
-        return int(kv["traffic_bytes_per_launch"].strip())
-    except (KeyError, ValueError):
-        return None
+        return {}
+    out = {}
+    for ln in lines:
+        if ln.startswith("leg "):
+            parts = ln.split()
+            out[parts[1]] = {k: float(v) for k, v in (p.split("=", 1) for p in parts[2:])}
+    return out
 
 
 def _rows(pattern):
@@ -160,44 +211,131 @@ def summarize_trace(d):
     return "\n".join(lines)
 
 
+def _segments(rows, key=None):
+    """Dispatch rows in dispatch order, split at the probe's marker fills (a torch fill of
+    an int32 tensor between legs): [segment][rows]."""
+    def did(r):
+        return int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)
+    by = {}
+    for r in rows:
+        by.setdefault(did(r), []).append(r)
+    segs, cur = [], None
+    for d in sorted(by):
+        name = by[d][0]["Kernel_Name"]
+        if "FillFunctor<int>" in name:
+            if cur is not None:
+                segs.append(cur)
+            cur = []
+        elif cur is not None:
+            cur.append(by[d])
+    if cur is not None:
+        segs.append(cur)
+    return segs
+
+
 def summarize_pmc(fetch_dir, write_dir):
-    """Traffic of the decode kernel per dispatch from a FETCH_SIZE run and a WRITE_SIZE
-    run of `bench.py --probe`, each scaled by what the counter reads for the plain
-    device copy of COPY_BYTES in the same run."""
-    def per_kernel(d, counter):
-        agg = {}
-        for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
-            if r["Counter_Name"] == counter:
-                agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return agg
-
-    def pick(agg, key):
-        vals = [v for k, vs in agg.items() if key in k for v in vs]
-        return vals
-
-    out = {}
+    """Traffic per forward of every decode leg from a FETCH_SIZE run and a WRITE_SIZE run
+    of `bench.py --probe decode`, each counter scaled by what it reads for the plain device
+    copy of COPY_BYTES (the first segment of the probe)."""
+    res = {}
     for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        agg = per_kernel(d, counter)
-        # the calibration copy: the dispatches that moved about COPY_BYTES
-        copies = [v for k, vs in agg.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs
-                  if v * 1024 > COPY_BYTES / 2]
-        kern = pick(agg, DECODE_KERNEL)
-        if not copies or not kern:
-            raise SystemExit(f"{counter}: calibration copy or decode kernel not found in {d}")
+        rows = [r for r in _rows(os.path.join(d, "**", "*counter_collection.csv")) if r["Counter_Name"] == counter]
+        segs = _segments(rows)
+        if len(segs) != 1 + len(DECODE_LEGS):
+            raise SystemExit(f"{counter}: {len(segs)} segments, expected {1 + len(DECODE_LEGS)}")
+        copies = [float(g[0]["Counter_Value"]) for g in segs[0] if "copy" in g[0]["Kernel_Name"].lower()]
+        copies = [v for v in copies if v * 1024 > COPY_BYTES / 2]
+        if not copies:
+            raise SystemExit(f"{counter}: calibration copy not found")
         copy_kib = float(np.median(copies))
         factor = (COPY_BYTES / 1024.0) / copy_kib
-        out[tag] = dict(copy_kib=copy_kib, factor=factor, kernel_kib=float(np.median(kern)), n=len(kern))
-    traffic = out["fetch"]["kernel_kib"] * 1024 * out["fetch"]["factor"] + \
-        out["write"]["kernel_kib"] * 1024 * out["write"]["factor"]
-    return out, int(round(traffic))
+        legs = {}
+        for (label, _, _), seg in zip(DECODE_LEGS, segs[1:]):
+            per_kernel = {}
+            for g in seg:
+                name = g[0]["Kernel_Name"]
+                if any(k in name for k in FORWARD_KERNELS):
+                    per_kernel.setdefault(name, []).append(sum(float(r["Counter_Value"]) for r in g))
+            legs[label] = dict(kib=sum(float(np.median(v)) for v in per_kernel.values()),
+                               kernels={k: len(v) for k, v in per_kernel.items()})
+        res[tag] = dict(copy_kib=copy_kib, factor=factor, legs=legs)
+    lines = []
+    for tag in ("fetch", "write"):
+        lines.append(f"{tag}: calibration copy {res[tag]['copy_kib']:.1f} KiB per dispatch for {COPY_BYTES // 1024} KiB "
+                     f"copied -> factor {res[tag]['factor']:.4f}")
+    import synthetic as S
+    for label, wname, M in DECODE_LEGS:
+        wl = S.WORKLOADS[wname]
+        f = res["fetch"]["legs"][label]
+        w = res["write"]["legs"][label]
+        fb = f["kib"] * 1024 * res["fetch"]["factor"]
+        wb = w["kib"] * 1024 * res["write"]["factor"]
+        ab = leg_bytes(wl, M)
+        kern = ";".join(f"{k.split('(')[0]}x{n}" for k, n in f["kernels"].items())
+        lines.append(f"leg {label} fetch_bytes={fb:.0f} write_bytes={wb:.0f} traffic_bytes={fb + wb:.0f} "
+                     f"alg_bytes={ab} ratio={(fb + wb) / ab:.4f}")
+        lines.append(f"  kernels of {label}: {kern}")
+    lines.append(f"source_sha256: {kernel_source_hash()}")
+    return "\n".join(lines)
 
 
-def time_forward(Q, pool, x, act, steps, warmup, use_graph=True, schedule=None, warm_s=0.0, reps=1):
-    """Average time (ms) of one forward over `steps` forwards, each on the next pool copy.
+def summarize_prefill(pmc_dir, trace_dir):
+    """Matrix-core busy fraction, engine clock and instruction mix per prefill leg from a
+    counter run and a trace run of `bench.py --probe prefill`."""
+    rows = _rows(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
+    segs = _segments(rows)
+    trows = _rows(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
+    tsegs = _segments(trows)
+    if len(segs) != len(PREFILL_LEGS) or len(tsegs) != len(PREFILL_LEGS):
+        raise SystemExit(f"{len(segs)} / {len(tsegs)} segments, expected {len(PREFILL_LEGS)}")
+    lines = []
+    for (label, _, M), seg, tseg in zip(PREFILL_LEGS, segs, tsegs):
+        main = [g for g in seg if "qgemm_lds_kernel" in g[0]["Kernel_Name"] or "qmm_kernel" in g[0]["Kernel_Name"]]
+        if not main:
+            raise SystemExit(f"{label}: no tile kernel dispatches")
+        cnt = {}
+        for g in main:
+            per = {}
+            for r in g:
+                per[r["Counter_Name"]] = per.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            for k, v in per.items():
+                cnt.setdefault(k, []).append(v)
+        med = {k: float(np.median(v)) for k, v in cnt.items()}
+        durs = sorted((int(g[0]["End_Timestamp"]) - int(g[0]["Start_Timestamp"])) / 1e3 for g in tseg
+                      if "qgemm_lds_kernel" in g[0]["Kernel_Name"] or "qmm_kernel" in g[0]["Kernel_Name"])
+        us = durs[len(durs) // 2]
+        cycles = med["GRBM_GUI_ACTIVE"] / XCDS
+        busy = med["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / cycles
+        ghz = cycles / (us * 1e3)
+        lines.append(f"leg {label} mfma_busy={busy:.4f} clock_ghz={ghz:.3f} kernel_us={us:.3f} "
+                     f"mfma_insts={med['SQ_INSTS_MFMA']:.0f} valu_per_mfma={(med['SQ_INSTS_VALU'] - med['SQ_INSTS_MFMA']) / med['SQ_INSTS_MFMA']:.3f} "
+                     f"lds_insts={med['SQ_INSTS_LDS']:.0f} lds_bank_conflict_cycles={med['SQ_LDS_BANK_CONFLICT']:.0f}")
+        lines.append(f"  kernel of {label}: {main[0][0]['Kernel_Name']} ({len(main)} dispatches)")
+    lines.append(f"source_sha256: {kernel_source_hash()}")
+    return "\n".join(lines)
 
-    With a graph: one untimed replay, then more untimed replays until warm_s seconds have
-    passed (so the clocks have settled under this load), then `reps` timed replays of the
-    `steps` forwards; the median replay is returned."""
+
+class Flush:
+    """Reads FLUSH_BYTES of device memory (four times the Infinity Cache), so that a
+    following forward finds nothing of its working set cached.  Queued without a wait:
+    the GPU is still busy with it while the host queues the timed work behind it."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = None
+
+    def __call__(self):
+        self.sink = self.buf.sum()
+
+
+def time_forward(Q, pool, x, act, steps, warmup, flush, use_graph=True, schedule=None, warm_s=0.0, reps=1):
+    """Average time (ms) of one forward over `steps` forwards, forward i on pool copy
+    i mod len(pool).
+
+    With a graph: one untimed replay, more untimed replays until warm_s seconds have
+    passed (so the clocks have settled under this load), then `reps` timed replays of
+    the `steps` forwards, each right behind a cache flush; the median replay is returned."""
     import torch
     pw0 = pool[0]
     M = x.shape[0]
@@ -211,6 +349,7 @@ def time_forward(Q, pool, x, act, steps, warmup, use_graph=True, schedule=None, 
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
+    times = []
     if use_graph:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -226,30 +365,44 @@ def time_forward(Q, pool, x, act, steps, warmup, use_graph=True, schedule=None, 
         while time.perf_counter() - t0 < warm_s:
             g.replay()
             torch.cuda.synchronize()
-        times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            flush()
             e0.record()
             g.replay()
             e1.record()
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1) / steps)
-        ms = sorted(times)[len(times) // 2]
         del g
     else:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(steps):
-            run(i)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-    return ms, out
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            flush()
+            e0.record()
+            for i in range(steps):
+                run(i)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / steps)
+    return sorted(times)[len(times) // 2], out
 
 
-def cpu_baseline(wl_name, M, seconds=10.0):
-    """The oracle as it stands (dequantise, then the float64 product) on host cores."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl_name, M, seconds=2.5, runs=3):
+    """The oracle as it stands on host cores, on the INT4 decode workload at M rows:
+    (i) dequantise then the float64 product on every call (the oracle's forward), the
+    reported value; (ii) the weight dequantised once, the float64 product only; (iii) the
+    same product in float32.  Each style: `runs` runs of about `seconds` each, the median."""
     import oracle as O
     import synthetic as S
     try:
@@ -259,61 +412,78 @@ def cpu_baseline(wl_name, M, seconds=10.0):
         threads = 1
     wl = S.WORKLOADS[wl_name]
     N, K, G = wl["N"], wl["K"], wl["group"]
-    w = S.weights(wl)
-    canon = O.quantize("int4", w, G, symmetric=wl["symmetric"])
+    canon = O.quantize("int4", S.weights(wl), G, symmetric=wl["symmetric"])
     x = S.activations(wl, M)
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        O.forward("int4", x, canon, K)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = (time.perf_counter() - t0) / n
+    dw = O.dequant("int4", canon, K)
+    x32 = np.asarray(x, dtype=np.float32)
+    styles = {
+        "dequantize_then_linear_f64": lambda: O.forward("int4", x, canon, K),
+        "predequantized_f64": lambda: O.linear_ref(x, dw),
+        "predequantized_f32": lambda: x32 @ dw.T,
+    }
     b = alg_bytes("int4", M, N, K, G, not wl["symmetric"])
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} full forwards (dequantise + float64 product) of the {N}x{K} INT4 weight at M={M}, "
-                      f"{dt * 1e3:.1f} ms each"}
+    res = {}
+    for name, fn in styles.items():
+        per = []
+        for _ in range(runs):
+            n, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                n += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            per.append((time.perf_counter() - t0) / n)
+        dt = statistics.median(per)
+        res[name] = {"ms": round(dt * 1e3, 3), "GB/s": round(b / dt / 1e9, 4)}
+    main = res["dequantize_then_linear_f64"]
+    return {"value": main["GB/s"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the {N}x{K} INT4 weight (zero-points, g128) at M={M}: median of {runs} runs of "
+                      f"~{seconds:g} s per style; value = dequantise + float64 product per call",
+            "styles": res, "cpu_model": _cpu_model(), "nproc": len(os.sched_getaffinity(0))}
 
 
 def probe(which="decode"):
-    """Counter-collection workload, no timing.  decode: a plain device copy of COPY_BYTES
-    (the calibration of FETCH_SIZE / WRITE_SIZE) and 20 dispatches of the decode step;
-    prefill: 20 dispatches of the codebook prefill (M = 2048)."""
+    """Counter-collection workloads, no timing; legs are separated by a marker fill.
+    decode: a plain device copy of COPY_BYTES three times (the calibration of FETCH_SIZE /
+    WRITE_SIZE), then 20 forwards of each decode leg; prefill: 20 forwards of each
+    prefill leg.  Each forward reads the next copy of a 1 GiB weight pool."""
     import torch
 
     import bit_weight_only_offline_amd as Q
     import synthetic as S
     torch.cuda.set_device(0)
-    if which == "prefill":
-        wl5 = S.WORKLOADS["cb4_prefill"]
-        pool5 = _pool(Q, "cb4", wl5["N"], wl5["K"], 0, True, 5, 256 << 20)
-        x5 = torch.from_numpy(S.activations(wl5, 2048)).cuda().to(torch.bfloat16)
-        out = torch.empty((2048, wl5["N"]), dtype=torch.bfloat16, device="cuda")
-        ws = torch.zeros(max(Q.workspace_bytes("cb4", 2048, wl5["N"], wl5["K"], 0), 256), dtype=torch.uint8,
-                         device="cuda")
-        for i in range(20):
-            Q.linear(x5, pool5[i % len(pool5)], out=out, workspace=ws)
+    marker = torch.empty(1, dtype=torch.int32, device="cuda")
+    legs = DECODE_LEGS if which == "decode" else PREFILL_LEGS
+    if which == "decode":
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        print(f"probe: codebook prefill M=2048 x20 ({Q.default_schedule('cb4', 2048, wl5['N'], wl5['K'], 0)})",
+        marker.fill_(0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    pools = {}
+    for i, (label, wname, M) in enumerate(legs):
+        wl = S.WORKLOADS[wname]
+        if wname not in pools:
+            pools.clear()
+            torch.cuda.empty_cache()
+            pools[wname] = _leg_pool(Q, wl, 7)
+        pool = pools[wname]
+        x = torch.from_numpy(S.activations(wl, M)).cuda().to(torch.bfloat16)
+        act = "swiglu" if wl.get("swiglu") else None
+        out = torch.empty((M, wl["N"]), dtype=torch.bfloat16, device="cuda")
+        ws = torch.zeros(max(Q.workspace_bytes(wl["fmt"], M, wl["N"], wl["K"], wl["group"], act), 256),
+                         dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        marker.fill_(i + 1)
+        for j in range(20):
+            Q.linear(x, pool[j % len(pool)], act=act, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"probe: {label} x20 ({Q.default_schedule(wl['fmt'], M, wl['N'], wl['K'], wl['group'], act)})",
               flush=True)
-        return
-    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    wl = S.WORKLOADS["int4_asym_decode"]
-    N, K, G = wl["N"], wl["K"], wl["group"]
-    pool = _pool(Q, "int4", N, K, G, False, 2, POOL_BYTES)
-    x = torch.from_numpy(S.activations(wl, 16)).cuda().to(torch.bfloat16)
-    out = torch.empty((16, N), dtype=torch.bfloat16, device="cuda")
-    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
-    for i in range(20):
-        Q.linear(x, pool[i % len(pool)], out=out, workspace=ws)
-    torch.cuda.synchronize()
-    print(f"probe: copy {COPY_BYTES} bytes x3, decode M=16 x20 "
-          f"(kernel sources sha256 {kernel_source_hash()})", flush=True)
+    print(f"probe: done (kernel sources sha256 {kernel_source_hash()})", flush=True)
 
 
 def main():
@@ -323,22 +493,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="also M = 1, 4, 8 and every other workload shape")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--probe", nargs="?", const="decode", choices=("decode", "prefill"))
+    ap.add_argument("--sweep", action="store_true", help="also the sweep workloads (see the module docstring)")
+    ap.add_argument("--cpu-seconds", type=float, default=2.5, help="seconds per CPU-baseline run (3 runs per style)")
+    ap.add_argument("--probe", choices=("decode", "prefill"))
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-prefill", nargs=2, metavar=("PMC_DIR", "TRACE_DIR"))
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
         return
     if args.summarize_pmc:
-        parts, traffic = summarize_pmc(*args.summarize_pmc)
-        for tag, v in parts.items():
-            print(f"{tag}: copy_kib_per_dispatch: {v['copy_kib']:.1f} (copied {COPY_BYTES // 1024} KiB), "
-                  f"factor {v['factor']:.4f}; decode_kib_per_dispatch (median of {v['n']}): {v['kernel_kib']:.1f}")
-        print(f"source_sha256: {kernel_source_hash()}")
-        print(f"traffic_bytes_per_launch: {traffic}")
+        print(summarize_pmc(*args.summarize_pmc))
+        return
+    if args.summarize_prefill:
+        print(summarize_prefill(*args.summarize_prefill))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the library runs on one GPU (it has no multi-GPU path); use --gpus 1", file=sys.stderr)
@@ -353,57 +522,70 @@ def main():
     import synthetic as S
     torch.cuda.set_device(0)
     use_graph = not args.no_graph
+    flush = Flush()
+    traffic = recorded(TRAFFIC_FILE)
+    pcount = recorded(PREFILL_COUNTERS_FILE)
 
-    # ---- the step: INT4 zero-point decode, M = 16 ----
-    wl = S.WORKLOADS["int4_asym_decode"]
-    N, K, G = wl["N"], wl["K"], wl["group"]
-    pool = _pool(Q, "int4", N, K, G, False, 2, POOL_BYTES)
-    n_copies = len(pool)
-    xs = S.activations(wl, 16)
-    x16 = torch.from_numpy(xs[:16]).cuda().to(torch.bfloat16)
-    sched = Q.default_schedule("int4", 16, N, K, G)
-    main_ms, _ = time_forward(Q, pool, x16, None, args.steps, args.warmup, use_graph)
-    b16 = alg_bytes("int4", 16, N, K, G, True)
-    value = b16 / (main_ms * 1e-3) / 1e9
-    sweep = {}
-    if args.sweep:
-        for M in (1, 4, 8):
-            x = torch.from_numpy(xs[:M]).cuda().to(torch.bfloat16)
-            ms, _ = time_forward(Q, pool, x, None, max(50, args.steps // 2), args.warmup, use_graph)
-            b = alg_bytes("int4", M, N, K, G, True)
-            sweep[str(M)] = {"us": round(ms * 1e3, 3), "GB/s": round(b / (ms * 1e-3) / 1e9, 1)}
-        sweep["16"] = {"us": round(main_ms * 1e3, 3), "GB/s": round(value, 1)}
-    del pool
+    # ---- decode legs; the step is the INT4 zero-point decode at M = 16 ----
+    decode = {}
+    main_ms = main_copies = None
+    pool, pool_name = None, None
+    for label, wname, M in DECODE_LEGS:
+        wl = S.WORKLOADS[wname]
+        if pool_name != wname:
+            pool = None
+            torch.cuda.empty_cache()
+            pool, pool_name = _leg_pool(Q, wl, 7), wname
+        x = torch.from_numpy(S.activations(wl, M)).cuda().to(torch.bfloat16)
+        act = "swiglu" if wl.get("swiglu") else None
+        if label == MAIN_LEG:
+            # exactly --steps forwards per timed replay, one timed replay
+            ms, _ = time_forward(Q, pool, x, act, args.steps, args.warmup, flush, use_graph, warm_s=AUX_WARM_S)
+            main_ms, main_copies = ms, len(pool)
+        else:
+            ms, _ = time_forward(Q, pool, x, act, max(20, len(pool)), 5, flush, use_graph, warm_s=AUX_WARM_S, reps=3)
+        b = leg_bytes(wl, M)
+        gbs = b / (ms * 1e-3) / 1e9
+        sch = Q.default_schedule(wl["fmt"], M, wl["N"], wl["K"], wl["group"], act)
+        decode[label] = {"us": round(ms * 1e3, 3), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "alg_bytes": b, "traffic": (int(traffic[label]["traffic_bytes"]) if label in traffic else None),
+                         "schedule": f"tile {sch.tile}, splits {sch.splits}"}
+    pool = None
+    torch.cuda.empty_cache()
+    main_leg = decode[MAIN_LEG]
+    value = main_leg["GB/s"]
+
+    # ---- prefill legs: the codebook workload ----
+    prefill = {}
+    for label, wname, M in PREFILL_LEGS:
+        wl = S.WORKLOADS[wname]
+        if pool_name != wname:
+            pool = None
+            torch.cuda.empty_cache()
+            pool, pool_name = _leg_pool(Q, wl, 5), wname
+        x = torch.from_numpy(S.activations(wl, M)).cuda().to(torch.bfloat16)
+        ms, _ = time_forward(Q, pool, x, None, max(20, len(pool)), 3, flush, use_graph, warm_s=AUX_WARM_S, reps=3)
+        fl = 2.0 * M * wl["N"] * wl["K"]
+        tf = fl / (ms * 1e-3) / 1e12
+        sch = Q.default_schedule(wl["fmt"], M, wl["N"], wl["K"], wl["group"])
+        c = pcount.get(label, {})
+        prefill[label] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                          "mfma_busy_counter": c.get("mfma_busy"), "clock_ghz_counter": c.get("clock_ghz"),
+                          "schedule": f"tile {sch.tile}, splits {sch.splits}"}
+    pool = None
     torch.cuda.empty_cache()
 
-    # ---- prefill: 4-bit codebook, 3072 x 3072, M = 2048 ----
-    wl5 = S.WORKLOADS["cb4_prefill"]
-    # every forward reads the next copy of a 1 GiB pool, all copies once per replay, so the
-    # weights come from HBM, not from the Infinity Cache
-    pool5 = _pool(Q, "cb4", wl5["N"], wl5["K"], 0, True, 5, POOL_BYTES)
-    x5 = torch.from_numpy(S.activations(wl5, 2048)).cuda().to(torch.bfloat16)
-    ms5, _ = time_forward(Q, pool5, x5, None, max(len(pool5), args.steps // 4), max(3, args.warmup // 4), use_graph,
-                          warm_s=AUX_WARM_S, reps=3)
-    fl = 2.0 * 2048 * wl5["N"] * wl5["K"]
-    tflops = fl / (ms5 * 1e-3) / 1e12
-    prefill = {"workload": "cb4 Lloyd-Max codebook 3072x3072, M=2048, bf16", "us": round(ms5 * 1e3, 2),
-               "TFLOP/s": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-               "schedule": repr(Q.default_schedule("cb4", 2048, wl5["N"], wl5["K"], 0))}
-    del pool5
-    torch.cuda.empty_cache()
-
+    use_graph_sweep = use_graph
     others = {}
     if args.sweep:
-        for name, M_list in (("mxfp4_up", (1, 16, 64)), ("mxfp4_down", (1, 16, 64)), ("int8_swiglu", (1, 16, 128)),
-                             ("cb4_prefill", (256,))):
+        for name, M_list in (("mxfp4_up", (64,)), ("mxfp4_down", (64,)), ("int8_swiglu", (128,))):
             w_ = S.WORKLOADS[name]
             fmt = w_["fmt"]
             pl = _pool(Q, fmt, w_["N"], w_["K"], w_["group"], True, 7, POOL_BYTES)
             for M in M_list:
                 xa = torch.from_numpy(S.activations(w_, M)).cuda().to(torch.bfloat16)
                 act = "swiglu" if w_.get("swiglu") else None
-                ms, _ = time_forward(Q, pl, xa, act, max(20, len(pl), args.steps // 4), 5, use_graph,
-                                     warm_s=AUX_WARM_S, reps=3)
+                ms, _ = time_forward(Q, pl, xa, act, max(20, len(pl)), 5, flush, use_graph_sweep, warm_s=AUX_WARM_S, reps=3)
                 b = alg_bytes(fmt, M, w_["N"], w_["K"], w_["group"], False, bool(act), w_.get("bias_std") is not None)
                 fl = 2.0 * M * w_["N"] * w_["K"]
                 others[f"{name}/M{M}"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
@@ -412,14 +594,14 @@ def main():
             torch.cuda.empty_cache()
         # the other weight formats at the codebook prefill's shape (3072 x 3072, M = 2048),
         # default schedules, weights from a pool as above
+        wl5 = S.WORKLOADS["cb4_prefill"]
         xp = torch.from_numpy(S.activations(wl5, 2048)).cuda().to(torch.bfloat16)
-        for fmt, G, sym in (("int4", 128, True), ("int4", 128, False), ("mxfp4", 32, True), ("int8", 256, True)):
-            pl = _pool(Q, fmt, wl5["N"], wl5["K"], G, sym, 8, POOL_BYTES)
-            ms, _ = time_forward(Q, pl, xp, None, max(20, len(pl), args.steps // 4), 5, use_graph,
-                                 warm_s=AUX_WARM_S, reps=3)
+        for fmt, Gf, sym in (("int4", 128, True), ("int4", 128, False), ("mxfp4", 32, True), ("int8", 256, True)):
+            pl = _pool(Q, fmt, wl5["N"], wl5["K"], Gf, sym, 8, POOL_BYTES)
+            ms, _ = time_forward(Q, pl, xp, None, max(20, len(pl)), 5, flush, use_graph_sweep, warm_s=AUX_WARM_S, reps=3)
             fl = 2.0 * 2048 * wl5["N"] * wl5["K"]
             tf = fl / (ms * 1e-3) / 1e12
-            others[f"{fmt}{'' if sym else '_asym'}_g{G}_3072/M2048"] = {
+            others[f"{fmt}{'' if sym else '_asym'}_g{Gf}_3072/M2048"] = {
                 "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
             del pl
             torch.cuda.empty_cache()
@@ -599,10 +781,12 @@ def main():
         del pw
         torch.cuda.empty_cache()
 
+
     cpu = None if args.no_cpu else cpu_baseline("int4_asym_decode", 16, args.cpu_seconds)
+    wl2 = S.WORKLOADS["int4_asym_decode"]
     rec = {
         "metric": "W4A16 linear: effective HBM GB/s at M=1-16; TFLOP/s + MFMA util at M=2048",
-        "value": round(value, 1),
+        "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -614,17 +798,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "int4 asym g128 decode linear, W 4096x4096 (fp16 scales, 4-bit zeros), "
-                               "X bf16 [16,4096], bf16 out", "M": 16, "N": N, "K": K, "group": G,
-                   "weight_pool_copies": n_copies, "hip_graph": use_graph, "schedule": repr(sched)},
-        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "kernel": "qgemv_kernel (INT4, zero-points, group 128)", "alg_bytes": b16,
-                     "us_per_launch": round(main_ms * 1e3, 3)},
+                               "X bf16 [16,4096], bf16 out", "M": 16, "N": wl2["N"], "K": wl2["K"],
+                   "group": wl2["group"], "weight_pool_copies": main_copies, "hip_graph": use_graph,
+                   "cache": "1 GiB read before the timed replay", "schedule": main_leg["schedule"]},
+        "roofline": {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": main_leg["traffic"],
+                     "kernel": "qgemv_kernel (INT4, zero-points, group 128)", "alg_bytes": main_leg["alg_bytes"],
+                     "us_per_launch": main_leg["us"]},
+        "decode": decode,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
-    if sweep:
-        rec["sweep"] = sweep
     if others:
         rec["others"] = others
     if quant:
