@@ -19,7 +19,7 @@ __all__ = [
     "PackedWeight", "packed_bytes", "quantize", "pack", "unpack", "dequant_tile", "workspace_bytes", "linear",
     "Schedule", "default_schedule", "tile_shapes", "workspace", "PackedExperts", "pack_experts",
     "grouped_workspace_bytes", "grouped_linear", "int8_addmm_", "quantize_activations", "a8_tile_shapes",
-    "a8_workspace_bytes", "linear_a8",
+    "a8_workspace_bytes", "linear_a8", "noalloc_scratch_bytes", "linear_noalloc",
 ]
 
 QL_INT4, QL_MXFP4, QL_INT8, QL_CB4 = 0, 1, 2, 3
@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
         L.qlinear_workspace_bytes_ex.restype = ci
         L.qlinear_workspace_bytes_ex.argtypes = [ci, i64, i64, i64, ci, ci, ctypes.POINTER(Schedule),
                                                  ctypes.POINTER(sz)]
+        L.qlinear_noalloc_scratch_bytes.restype = sz
+        L.qlinear_noalloc_scratch_bytes.argtypes = []
+        L.qlinear_forward_noalloc.restype = ci
+        L.qlinear_forward_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, ci, ci, ci, vp, ci, vp, ci, vp]
         L.qlinear_forward_ex.restype = ci
         L.qlinear_forward_ex.argtypes = [vp, i64, i64, i64, vp, vp, vp, ci, ci, ci, vp, ci, vp, ci, vp, sz,
                                          ctypes.POINTER(Schedule), vp]
@@ -393,6 +397,43 @@ def linear(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, 
                                     1 if out_dtype == torch.float32 else 0,
                                     _ptr(workspace) if ws_need else None, ws_need if ws_need else 0,
                                     _sched(schedule), _stream(x.device)), "qlinear_forward")
+    return out.reshape(*lead, pw.N)
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the library's per-GPU scratch that linear_noalloc() uses as workspace."""
+    return int(lib().qlinear_noalloc_scratch_bytes())
+
+
+def linear_noalloc(x: torch.Tensor, pw: PackedWeight, bias: torch.Tensor | None = None, act=None,
+                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """linear() through qlinear_forward_noalloc: the library's per-GPU scratch serves as
+    workspace, so the call itself allocates nothing on the device (pass `out` to keep the
+    wrapper from allocating the output).  Calls that overlap on one GPU share the scratch."""
+    if x.requires_grad or (bias is not None and bias.requires_grad):
+        raise QLinearError("inference-only operator: inputs must not require grad")
+    if x.device.type != "cuda" or pw.w.device.type != "cuda":
+        raise QLinearError("the library runs on a HIP device only")
+    if x.dtype != torch.bfloat16:
+        raise QLinearError("x must be bfloat16")
+    act_id = _ACT[act]
+    width = 2 * pw.K if act_id == 1 else pw.K
+    if x.shape[-1] != width or not x.is_contiguous():
+        raise QLinearError(f"x must be a contiguous [..., {width}] tensor")
+    lead = x.shape[:-1]
+    M = x.numel() // width
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != pw.N):
+        raise QLinearError("bias must be bfloat16 [N]")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise QLinearError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=out_dtype, device=x.device)
+    elif out.dtype != out_dtype or out.numel() != M * pw.N or not out.is_contiguous() or out.device != x.device:
+        raise QLinearError("out must be a contiguous [M, N] tensor of out_dtype on x's device")
+    _check(lib().qlinear_forward_noalloc(_ptr(x), M, pw.N, pw.K, _ptr(pw.w), _ptr(pw.s), _ptr(pw.aux), pw.fmt,
+                                         pw.group, pw.has_zeros, _ptr(bias), act_id, _ptr(out),
+                                         1 if out_dtype == torch.float32 else 0, _stream(x.device)),
+           "qlinear_forward_noalloc")
     return out.reshape(*lead, pw.N)
 
 

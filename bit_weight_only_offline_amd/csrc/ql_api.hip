@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/qlinear.h"
 #include "ql_common.hpp"
 #include "ql_decode.hpp"
@@ -506,3 +508,72 @@ ql_status qlinear_grouped_forward(const void *x, int64_t T, const int32_t *token
 }
 
 }  // extern "C"
+
+// ---- allocation-free forward ---------------------------------------------------------
+// Scratch of qlinear_forward_noalloc: a file-scope device array in place of the caller's
+// workspace (split-K partial sums, the materialised SwiGLU input).  Every GPU the library
+// runs on holds its own copy, from module load until the process ends.  Host code never
+// uses the array's name as an address: the per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+namespace {
+
+constexpr size_t SCRATCH_BYTES = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 256;
+std::mutex scratch_mu;
+void *scratch_dev[SCRATCH_MAX_DEVICES] = {};
+
+// This device's copy of `scratch`, or null when the device cannot be determined, the
+// stream belongs to another device than the current one, or the lookup fails.
+void *device_scratch(hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return nullptr;
+    if (stream) {
+        hipDevice_t sd = -1;
+        if (hipStreamGetDevice(stream, &sd) != hipSuccess || int(sd) != dev) return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        scratch_dev[dev] = p;
+    }
+    return scratch_dev[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qlinear_noalloc_scratch_bytes(void) { return SCRATCH_BYTES; }
+
+ql_status qlinear_forward_noalloc(const void *x, int64_t M, int64_t N, int64_t K, const void *packed_w,
+                                  const void *packed_s, const void *packed_aux, ql_format f, int group,
+                                  int has_zeros, const void *bias, ql_act act, void *out, ql_dtype out_dtype,
+                                  void *stream) {
+    size_t need = 0;
+    ql_status st = check_format(f, N, K, group, has_zeros);
+    if (st != QL_OK) return st;
+    if (act != QL_ACT_NONE && act != QL_ACT_SWIGLU) return QL_E_ARG;
+    if (M < 0 || M >= (int64_t(1) << 31)) return QL_E_SHAPE;
+    if (M > 0) {
+        Layout L;
+        Plan p;
+        st = plan_for(f, M, N, K, group, has_zeros, act, nullptr, &L, &p);
+        if (st != QL_OK) return st;
+        need = p.ws_bytes;
+    }
+    if (need > SCRATCH_BYTES) return QL_E_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        ws = device_scratch((hipStream_t)stream);
+        if (!ws) return QL_E_HIP;
+    }
+    // the same validation and kernels as qlinear_forward(), with the scratch as workspace
+    return qlinear_forward_ex(x, M, N, K, packed_w, packed_s, packed_aux, f, group, has_zeros, bias, act, out,
+                              out_dtype, ws, need, nullptr, stream);
+}
+
+}  // extern "C"
+

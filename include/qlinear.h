@@ -254,6 +254,28 @@ ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * qlinear_forward() without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Arguments, validation, kernels and results are those of
+ * qlinear_forward(), bit for bit; the workspace is a device array of the library,
+ * qlinear_noalloc_scratch_bytes() bytes (64 MiB), one copy per GPU, held from the
+ * library's load until the process ends.  The call allocates nothing.
+ *   - Shapes whose workspace (qlinear_workspace_bytes()) exceeds the scratch are refused
+ *     with QL_E_WORKSPACE before any launch.
+ *   - The stream must belong to the current device (QL_E_HIP otherwise); the scratch's
+ *     device address is looked up on the first call on each device.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ *     contents (no call depends on them): calls that may overlap on one GPU (two
+ *     streams, two threads) race on it and must be ordered by the caller.
+ */
+size_t qlinear_noalloc_scratch_bytes(void);
+ql_status qlinear_forward_noalloc(const void *x, int64_t M, int64_t N, int64_t K,
+                                  const void *packed_w, const void *packed_s, const void *packed_aux,
+                                  ql_format f, int group, int has_zeros,
+                                  const void *bias, ql_act act, void *out, ql_dtype out_dtype,
+                                  void *stream);
+
+/*
  * Explicit schedules, for tuning.  CDNA kernels are sensitive to tile shapes (Petit
  * package description, "Known limitations"), so the schedule that qlinear_forward()
  * picks can be inspected and overridden.
