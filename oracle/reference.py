@@ -243,6 +243,59 @@ def lloyd_max_gaussian(levels: int = 16, tol: float = 1e-15, iters: int = 200000
     return cent, thr
 
 
+def _bf16_value(bits: int) -> float:
+    """Value of a non-negative bf16 bit pattern; the pattern after the largest finite
+    value (the infinity) stands for 2^128, the next power of two, so that the midpoint
+    between them is the overflow threshold of round-to-nearest."""
+    if bits >= 0x7F80:
+        return 2.0 ** 128
+    return float(np.array([bits << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+def row_norm_bf16(w) -> np.ndarray:
+    """bf16 of the exact Euclidean norm of each row, rounded once (nearest, ties to the
+    even bf16 value): the norm that no summation order changes.
+
+    The square of a float32 value is exact in float64, and math.fsum returns the
+    correctly rounded float64 s of the exact sum S of the squares.  The bf16 value of
+    sqrt(S) is decided by where S lies against the squares of the midpoints m between
+    neighbouring bf16 values; a midpoint has 9 significant bits, so m^2 is exact in
+    float64.  Rounding is monotonic and m^2 is representable, so s > m^2 implies S > m^2
+    and s < m^2 implies S < m^2; only s == m^2 needs S itself, summed in exact rational
+    arithmetic.  S == m^2 means sqrt(S) == m: a tie, resolved to the even value."""
+    from fractions import Fraction
+    w = np.asarray(w, dtype=np.float32)
+    out = np.zeros(w.shape[0], dtype=np.float32)
+    for n in range(w.shape[0]):
+        sq = w[n].astype(np.float64) ** 2
+        s = math.fsum(sq)
+        if s == 0.0:
+            continue
+        exact = None
+
+        def cmp(m2: float) -> int:          # sign of S - m2
+            nonlocal exact
+            if s != m2:
+                return 1 if s > m2 else -1
+            if exact is None:
+                exact = sum((Fraction(float(v)) for v in sq), Fraction(0))
+            return (exact > Fraction(m2)) - (exact < Fraction(m2))
+
+        b = int(bf16_bits(bf16_from_f64(np.array([math.sqrt(s)])))[0])   # a neighbour of the answer
+        while True:
+            hi = 0x7F80 if b >= 0x7F80 else b + 1
+            c_hi = -1 if b >= 0x7F80 else cmp(((_bf16_value(b) + _bf16_value(hi)) / 2) ** 2)
+            c_lo = 1 if b == 0 else cmp(((_bf16_value(b - 1) + _bf16_value(b)) / 2) ** 2)
+            if c_hi > 0 or (c_hi == 0 and b & 1):
+                b = hi
+            elif c_lo < 0 or (c_lo == 0 and b & 1):
+                b = b - 1
+            else:
+                break
+        out[n] = np.inf if b >= 0x7F80 else np.float32(_bf16_value(b))
+    return out
+
+
 def quantize_cb4(w, centroids, norms=None):
     """-> (indices uint8 [N,K] in 0..15, row norms: bf16-valued float32 [N]).
 
@@ -251,7 +304,7 @@ def quantize_cb4(w, centroids, norms=None):
     N, K = w.shape
     c32 = np.asarray(centroids, dtype=np.float32)
     if norms is None:
-        nrm = bf16_from_f64(np.sqrt(np.sum(w.astype(np.float64) ** 2, axis=1)))
+        nrm = row_norm_bf16(w)
     else:
         nrm = np.asarray(norms, dtype=np.float32)
     rk = np.float32(math.sqrt(K))

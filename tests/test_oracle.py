@@ -270,6 +270,63 @@ def test_cb4_requantise_with_norms_and_ties():
     assert n4[0] == 0 and np.all(O.dequant_cb4(O.pack_nibbles(i4), n4, c, 64) == 0)
 
 
+def _bf16_of_sqrt_by_decimal(row) -> float:
+    """Independent check of the codebook norm: sqrt of the exact sum of squares to 120
+    decimal digits (exact when the sum is a perfect square), then the nearest bf16 value
+    by direct distance among the three candidates around a first guess, ties to the even
+    encoding."""
+    from decimal import Decimal, getcontext
+    from fractions import Fraction
+    getcontext().prec = 120
+    S = sum((Fraction(float(v)) ** 2 for v in row), Fraction(0))
+    if S == 0:
+        return 0.0
+    root = (Decimal(S.numerator) / Decimal(S.denominator)).sqrt()
+    guess = int(O.bf16_bits(O.bf16_from_f64(np.array([float(root)])))[0])
+    best = None
+    for b in (guess - 1, guess, guess + 1):
+        if b < 0 or b > 0x7F7F:
+            continue
+        v = Decimal(float(np.array([b << 16], dtype=np.uint32).view(np.float32)[0]))
+        d = abs(v - root)
+        if best is None or d < best[0] or (d == best[0] and b % 2 == 0):
+            best = (d, b)
+    return float(np.array([best[1] << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+def test_cb4_norm_is_exact_bf16_of_row_norm():
+    """The codebook norm is the bf16 of the exact Euclidean norm, rounded once: pinned to
+    a 120-digit decimal square root on random rows and on rows built to sit exactly on,
+    just above and just below a rounding midpoint, where a float64 sum of the squares is
+    ambiguous; a permuted row gives the same norm."""
+    rng = np.random.default_rng(44)
+    rows = [(rng.standard_normal(37) * 0.02).astype(np.float32) for _ in range(6)]
+    m = np.float32(1.0 + 3 * 2 ** -8)                 # midpoint of bf16 1+2^-7 and 1+2^-6 ... odd/even pair
+    rows.append(np.array([m], dtype=np.float32))      # sqrt(S) == midpoint: tie to even
+    rows.append(np.array([m, 2.0 ** -60], dtype=np.float32))    # just above: float64 sum cannot see it
+    rows.append(np.array([np.nextafter(m, np.float32(0))], dtype=np.float32))   # just below
+    m2 = np.float32(1.0 + 2 ** -8)                    # midpoint of 1 and 1+2^-7
+    rows.append(np.array([m2], dtype=np.float32))
+    rows.append(np.array([m2, 2.0 ** -70], dtype=np.float32))
+    rows.append(np.array([3.0, 4.0] + [0.0] * 5, dtype=np.float32))             # exactly 5
+    rows.append(np.array([1e-30, 3e-31], dtype=np.float32))                     # tiny squares
+    rows.append(np.array([3e38, 3e38, 3e38, 3e38], dtype=np.float32))           # norm beyond bf16 max
+    K = max(len(r) for r in rows)
+    w = np.zeros((len(rows), K), dtype=np.float32)
+    for i, r in enumerate(rows):
+        w[i, :len(r)] = r
+    got = O.row_norm_bf16(w)
+    for i, r in enumerate(rows[:-1]):
+        assert got[i] == _bf16_of_sqrt_by_decimal(r), (i, got[i])
+    assert np.isinf(got[-1])
+    assert got[6] == np.float32(1.0 + 2 ** -6)        # tie -> even encoding
+    assert got[7] == np.float32(1.0 + 2 ** -6) and got[8] == np.float32(1.0 + 2 ** -7)
+    assert got[9] == np.float32(1.0) and got[10] == np.float32(1.0 + 2 ** -7)
+    assert got[11] == np.float32(5.0)
+    perm = rows[0][rng.permutation(len(rows[0]))]
+    assert O.row_norm_bf16(perm[None, :])[0] == got[0]
+
+
 def test_cb4_norm_is_rounded_row_norm():
     rng = np.random.default_rng(10)
     w = (rng.standard_normal((4, 300)) * 0.02).astype(np.float32)
