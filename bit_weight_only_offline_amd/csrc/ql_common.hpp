@@ -132,7 +132,7 @@ struct TileCfg { int kind, MT, NT, SK, PF, WK, WM, WN; };
 constexpr int NUM_TILE_CFGS = 22;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {0, 1, 1, 0, 4, 8, 1, 1}, {0, 1, 2, 0, 4, 8, 1, 1}, {0, 1, 4, 0, 4, 4, 1, 1}, {0, 1, 1, 0, 8, 4, 1, 1},
-    {2, 2, 3, 0, 4, 2, 1, 2}, {2, 1, 3, 0, 4, 2, 2, 2}, {2, 1, 3, 0, 4, 1, 2, 2}, {2, 2, 3, 0, 4, 1, 1, 4},
+    {2, 2, 3, 0, 4, 2, 1, 2}, {2, 2, 2, 0, 4, 2, 1, 4}, {2, 4, 3, 0, 4, 2, 1, 2}, {2, 4, 2, 0, 4, 2, 1, 4},
     {2, 8, 3, 0, 3, 1, 1, 4}, {2, 8, 4, 0, 3, 1, 1, 4}, {2, 4, 4, 0, 3, 1, 2, 2}, {2, 4, 3, 0, 4, 1, 1, 4},
     {2, 2, 4, 0, 4, 1, 1, 4}, {2, 8, 3, 0, 3, 2, 1, 4}, {2, 8, 4, 0, 3, 2, 1, 4}, {2, 4, 4, 0, 4, 2, 1, 4},
     {2, 4, 3, 0, 4, 2, 1, 4}, {2, 2, 4, 0, 6, 1, 1, 4}, {2, 4, 3, 0, 5, 1, 1, 4},
@@ -144,10 +144,11 @@ constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
 __host__ __device__ constexpr int cfg_rows(const TileCfg &t) { return 16 * t.MT * (t.kind == 2 ? t.WM : 1); }
 __host__ __device__ constexpr int cfg_ntiles(const TileCfg &t) { return t.kind == 0 ? t.NT : t.NT * t.WN; }
 // One stage of a decode wavefront's LDS ring: NT packed weight tiles, the chunk's
-// scale words and zero-point words (256-byte blocks), then the activation block of 16
-// rows x one chunk of bf16; with the fused SwiGLU input stage (sw), one more 1 KiB
-// block for the gate rows (the up rows go to the activation block, where h replaces
-// them).
+// scale words and zero-point words (256-byte blocks), then the activation block: 16
+// rows x one chunk of bf16, or for batches that fit one activation load (xr = rows per
+// load, small batches) just that load's 1 KiB; with the fused SwiGLU input stage (sw,
+// always a one-load block), one more 1 KiB block for the gate rows (the up rows go to
+// the activation block, where h replaces them).
 __host__ __device__ constexpr int gemv_spc(int fmt, int gs) {
     return (fmt == FMT_INT4 || fmt == FMT_INT8) ? (gs <= chunk_k(fmt) / 32 ? chunk_k(fmt) / 32 / gs : 1) : 1;
 }
@@ -158,19 +159,25 @@ __host__ __device__ constexpr int gemv_scale_blocks(int fmt, int gs, int nt) {
 __host__ __device__ constexpr int gemv_zero_blocks(int fmt, bool zp, int gs, int nt) {
     return (fmt == FMT_INT4 && zp) ? (nt * gemv_spc(fmt, gs) * 2 + 63) / 64 : 0;
 }
-__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt, bool sw = false) {
+// activation rows of one 1 KiB load: 64 16-byte pieces, chunk_k(fmt) / 8 pieces a row
+__host__ __device__ constexpr int gemv_rows_per_load(int fmt) { return 64 / (chunk_k(fmt) / 8); }
+__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt, bool sw = false,
+                                                   bool small = false) {
     return nt * TILE_BYTES + 256 * (gemv_scale_blocks(fmt, gs, nt) + gemv_zero_blocks(fmt, zp, gs, nt)) +
-           16 * chunk_k(fmt) * 2 + (sw ? 1024 : 0);
+           ((small || sw) ? 1024 : 16 * chunk_k(fmt) * 2) + (sw ? 1024 : 0);
 }
 constexpr int LDS_BYTES_MAX = 160 * 1024;
-// ring depth: PF stages per wavefront, fewer if they would not fit the LDS
-__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
-    return pf * wk * gemv_stage_bytes(fmt, zp, gs, nt, sw) <= LDS_BYTES_MAX
-               ? pf
-               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt, sw));
+// ring depth: PF stages per wavefront (one more for the one-load activation block, up
+// to 8), fewer if they would not fit the LDS
+__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false,
+                                                  bool small = false) {
+    return ((small || sw) && pf < 8 ? pf + 1 : pf) * wk * gemv_stage_bytes(fmt, zp, gs, nt, sw, small) <= LDS_BYTES_MAX
+               ? ((small || sw) && pf < 8 ? pf + 1 : pf)
+               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt, sw, small));
 }
-__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
-    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf, sw) * gemv_stage_bytes(fmt, zp, gs, nt, sw);
+__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false,
+                                                 bool small = false) {
+    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf, sw, small) * gemv_stage_bytes(fmt, zp, gs, nt, sw, small);
 }
 // LDS of a ring schedule: PF stages of activations + packed tiles + every wavefront's
 // scale and zero-point words, or, when WK > 1, the hand-over of one k-half's
@@ -208,12 +215,18 @@ constexpr int SWIGLU_FUSE_MAX_M = 2;
 
 inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 
-// Default schedule by batch size (measured on MI355X over the workload shapes):
+// Default schedule by batch size (measured on MI355X, weights read from HBM, over the
+// workload shapes and 3072^2 / 8192^2 / 28672 x 4096 weights of every format):
 //   M <= 16      decode kernel, more column tiles per wavefront for wide layers;
-//   M <= 64      32 x 256 ring tiles, split-K to fill the machine;
-//   M <= 256     64-row ring tiles, two wavefronts per tile (INT8: 256 columns);
-//   larger M     128 x 192 ring tiles, two wavefronts per tile (INT formats, whose
-//                group accumulators need the registers: one wavefront per tile).
+//   M <= 32      32 x 96 ring tiles (four wavefronts, two k-halves);
+//   M <= 64      64 x 128 ring tiles (eight wavefronts);
+//   then         weights that stay in the caches (under 16 MiB): 32 x 96 tiles up to
+//                M = 512; weights streamed from HBM: 64-row tiles with two k-halves up
+//                to M = 1024 (INT8: 64 x 256 with a four-deep ring, else 64 x 256 with a
+//                two-deep ring);
+//   larger M     128 x 192 ring tiles, two wavefronts per tile (INT4: one wavefront per
+//                tile, whose group accumulators need the registers).
+// Split-K is added by make_plan when the tiles alone do not fill the machine.
 // Decode schedule: the one whose busiest compute unit streams the fewest column tiles,
 // counting one resident workgroup per CU (256 CUs), ties to the wider schedule (fewer
 // rounds of workgroups).  Candidates in order of columns per workgroup: 1, 2, 3, 4, 7.
@@ -234,19 +247,13 @@ inline int decode_cfg(int64_t ntiles) {
 
 inline int default_cfg(const Layout &L, int64_t M) {
     if (M <= 16) return decode_cfg(L.ntiles);
-    if (M <= 64) return 12;
-    const bool intf = L.fmt == FMT_INT4 || L.fmt == FMT_INT8;
-    // weights streamed from HBM (16 MiB and more) take 64 x 256 tiles up to M = 1024:
-    // with a two-deep ring (measured 1.3-1.9x faster than 64 x 192 at M = 128-256 and
-    // up to 1.35x faster than 128 x 192 at M = 512-1024, from 29 MB up), INT8 with its
-    // four-deep ring; smaller, cache-resident weights keep 64 x 192 up to M = 256
+    if (M <= 32) return 4;
+    if (M <= 64) return 7;
     const bool streamed = L.w_bytes >= (size_t(16) << 20);
-    if (M <= 256 || (streamed && M <= 1024)) {
-        if (L.fmt == FMT_INT8) return 15;
-        return streamed ? 21 : 16;
-    }
+    if (!streamed && M <= 512) return 4;
+    if (streamed && M <= 1024) return L.fmt == FMT_INT8 ? 15 : 21;
     if (L.fmt == FMT_INT8) return 13;
-    return intf ? 8 : 13;
+    return L.fmt == FMT_INT4 ? 8 : 13;
 }
 
 // splits <= 0 picks the split count automatically (tile schedules only): enough

@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     constexpr int NA = A_BYTES / 1024;              // wave-wide A loads per stage
     constexpr int NB = NTT;                         // wave-wide B loads per stage
 
-    static_assert(S >= 2 && S <= 6, "ring depth");
+    static_assert(S >= 2 && S <= 8, "ring depth");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -289,7 +289,6 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
             for (int tt = 0; tt < SPW; ++tt)
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt) afs[tt][mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt][mt]);
-            __builtin_amdgcn_sched_barrier(0);     // keep the reads ahead of the MFMAs
         }
 #pragma unroll
         for (int tt = 0; tt < SPW; ++tt) {
@@ -359,6 +358,24 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 }
             }
         }
+        if constexpr (!INTF) {
+            // Interleave the register decode with the MFMAs: the first tile's decode, then
+            // each MFMA followed by up to two VALU instructions, so that one wavefront
+            // keeps the matrix pipe fed while it decodes the next tile (left to itself
+            // the scheduler emits the MFMAs in bursts and the VALU work between them)
+            // The first k-step's A fragments are read up front; the later k-steps' reads
+            // are spread over the first k-step's MFMAs.
+            constexpr int NMF = SPW * NTW * MTW * (SPLIT ? 2 : 1);
+            constexpr int NRD = (SPW - 1) * MTW;             // fragment reads after the first k-step's
+            __builtin_amdgcn_sched_group_barrier(0x100, MTW + NTW, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
     };
 
     // ---- prologue: stages 0 .. S-2 in flight ----
@@ -375,7 +392,9 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 if (i < nck) {
                     // loads issued after chunk i's: those of chunks i+1 .. min(i+S-2, nck-1)
                     const int later = min(S - 2, nck - 1 - i);
-                    if (later >= 4) wait_vmcnt<4 * PER_STAGE>();
+                    if (later >= 6) wait_vmcnt<6 * PER_STAGE>();
+                    else if (later == 5) wait_vmcnt<5 * PER_STAGE>();
+                    else if (later == 4) wait_vmcnt<4 * PER_STAGE>();
                     else if (later == 3) wait_vmcnt<3 * PER_STAGE>();
                     else if (later == 2) wait_vmcnt<2 * PER_STAGE>();
                     else if (later == 1) wait_vmcnt<PER_STAGE>();

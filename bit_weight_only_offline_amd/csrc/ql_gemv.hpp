@@ -15,6 +15,11 @@
 // the epilogue applies the codebook row scale and the bias and rounds to bf16.  No
 // workspace, no cross-workgroup traffic.
 //
+// Batches that fit one activation load (SMALL: up to 4 rows for the 4-bit formats, 8 for
+// INT8) hold only that load's 1 KiB per stage, which leaves room for one more stage in
+// flight; the A fragments of rows past the load read its rows again (rows at or beyond M
+// never reach a stored output).
+//
 // Fused SwiGLU input stage (SW, batches of at most SWIGLU_FUSE_MAX_M rows): the stage
 // receives the up rows in the activation block and the gate rows in one more block, and
 // the wavefront replaces each up value by h = bf16(up * silu(gate)) in LDS before it
@@ -36,7 +41,7 @@
 
 namespace ql {
 
-template <int FMT, bool ZP, int GS, int NT, int WK, int PF, bool SW>
+template <int FMT, bool ZP, int GS, int NT, int WK, int PF, bool SW, bool SMALL>
 __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int CH = chunk_k(FMT);
     constexpr int STEPS = CH / 32;
@@ -48,10 +53,13 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int S_OFF = NT * TILE_BYTES;
     constexpr int Z_OFF = S_OFF + 256 * NSS;
     constexpr int X_OFF = Z_OFF + 256 * NSZ;
-    constexpr int G_OFF = X_OFF + XB::BYTES;         // gate rows (SW)
-    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT, SW);
-    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF, SW);
+    constexpr bool ONE = SW || SMALL;                 // a one-load activation block
+    constexpr int NI = ONE ? 1 : XB::NI;              // activation loads a stage holds
+    constexpr int G_OFF = X_OFF + NI * 1024;          // gate rows (SW)
+    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT, SW, SMALL);
+    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF, SW, SMALL);
     static_assert(G_OFF + (SW ? 1024 : 0) == STAGE && S >= 1 && S <= 8, "stage layout");
+    static_assert(gemv_rows_per_load(FMT) == XB::RPI, "rows per activation load");
     // fused SwiGLU: the batch's rows fit the first activation load; each lane forms HE
     // consecutive h values of one row
     constexpr int HE = SWIGLU_FUSE_MAX_M * CH / 64;
@@ -102,11 +110,11 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
 
     // ---- per-lane parts of the loads ----
     // activation loads actually issued: those holding a row below M (wave-uniform)
-    const int nia = min(XB::NI, (a.M + XB::RPI - 1) / XB::RPI);
-    uint32_t xrow[XB::NI];
-    int xk[XB::NI];
+    const int nia = min(NI, (a.M + XB::RPI - 1) / XB::RPI);
+    uint32_t xrow[NI];
+    int xk[NI];
 #pragma unroll
-    for (int j = 0; j < XB::NI; ++j) {
+    for (int j = 0; j < NI; ++j) {
         const int r = j * XB::RPI + lane / XB::P;
         const int pc = (lane % XB::P) ^ XB::xswz(r);
         xrow[j] = (r < a.M) ? uint32_t(r) * uint32_t(a.ldx) * 2u : 0x80000000u;   // bit 31: not fetched
@@ -116,7 +124,7 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     uint32_t xfrag[STEPS];
 #pragma unroll
     for (int t = 0; t < STEPS; ++t)
-        xfrag[t] = uint32_t(X_OFF + XB::slot(c, 4 * t + g));
+        xfrag[t] = uint32_t(X_OFF + XB::slot(ONE ? c % XB::RPI : c, 4 * t + g));
     // scale / zero-point words: word e of a chunk's scale block is word (e % 8) of the
     // record of tile e / (8 SPC), group slot (e / 8) % SPC (MXFP4: column e % 16 of tile
     // e / 16); zero-point words likewise with 2 words per record
@@ -177,7 +185,7 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
             ld32_lds(zr, off, base + Z_OFF + d * 256);
         }
 #pragma unroll
-        for (int j = 0; j < XB::NI; ++j) {
+        for (int j = 0; j < NI; ++j) {
             if (j < nia) {
                 const int k = kc * CH + xk[j];
                 const uint32_t past_k = uint32_t(~(int32_t(k - a.K) >> 31)) & 0x80000000u;   // k >= K

@@ -14,7 +14,8 @@
 //   MXFP4            e = floor(log2 amax) - 2 clamped to [-127, 127] (0 for an all-zero
 //                    block), element = nearest E2M1 value of w * 2^-e, ties to the even
 //                    code, saturating at 6, no negative zero; scale code e + 127
-//   codebook         norm = bf16 of the float64 row norm (one rounding),
+//   codebook         norm = bf16 of the exact row norm (the exact sum of the squares,
+//                    one correctly rounded bf16 square root, ties to even),
 //                    u = (w * fp32(sqrt K)) / norm, index = nearest level (distances in
 //                    float64), ties to the lower index
 // A scale that rounds to zero gives codes 0 (and zero-point 0).
@@ -170,34 +171,155 @@ struct Levels { float c[16]; };
 
 // float64 -> bf16, one rounding to 8 significant bits with ties to even (the spacing
 // stops shrinking below the float32 normal range); finite non-negative input
-__device__ inline float bf16_from_double(double a) {
+__host__ __device__ inline float bf16_from_double(double a) {
     if (!(a > 0.0)) return 0.0f;
     int e;
     frexp(a, &e);                                        // a in [2^(e-1), 2^e)
-    const int q = max(e, -125) - 8;
+    const int q = (e > -125 ? e : -125) - 8;
     return (float)ldexp(rint(ldexp(a, -q)), q);
 }
 
-// One workgroup (256 threads) per row: the row norm in float64, reduced over the
-// threads in a fixed order, then the indices of the element pairs.
+// ---- exact sum of float32 squares --------------------------------------------------------
+// A float32 |w| = m * 2^(f - 150) with m < 2^24 and f = max(biased exponent, 1), so
+// w^2 = m^2 * 2^(2f - 300) with m^2 < 2^48.  Relative to the row's largest f (F), the
+// squares are summed as integers on a 320-bit grid (five 64-bit limbs) whose unit is
+// 2^(2F - 300 - SQ_SHIFT): the largest square sits at bits 241..288, and 2^30 of them
+// stay below bit 319.  Bits of a square that fall below the grid only set a sticky flag
+// (the sum is then strictly above the grid value).  Integer addition is associative, so
+// the result does not depend on the order of the additions.
+constexpr int SQ_SHIFT = 241;
+struct Sum320 {
+    uint64_t l[5];
+    uint32_t sticky;
+};
+
+__host__ __device__ inline void add320(Sum320 &a, const Sum320 &b) {
+    uint64_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const uint64_t t = a.l[i] + c;
+        const uint64_t c1 = t < c;
+        a.l[i] = t + b.l[i];
+        c = c1 + (a.l[i] < t);
+    }
+    a.sticky |= b.sticky;
+}
+
+// add v * 2^shift (v < 2^48) to the accumulator; shift <= SQ_SHIFT
+__host__ __device__ inline void add_shifted(Sum320 &a, uint64_t v, int shift) {
+    if (shift < 0) {
+        const int d = -shift;
+        if (d >= 48) {
+            a.sticky |= v != 0;
+            return;
+        }
+        a.sticky |= (v & ((uint64_t(1) << d) - 1)) != 0;
+        v >>= d;
+        shift = 0;
+    }
+    const int q = shift >> 6, r = shift & 63;
+    const uint64_t lo = v << r, hi = r ? (v >> (64 - r)) : 0;
+    uint64_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const uint64_t add = (i == q) ? lo : ((i == q + 1) ? hi : 0);
+        const uint64_t t = a.l[i] + c;
+        const uint64_t c1 = t < c;
+        a.l[i] = t + add;
+        c = c1 + (a.l[i] < t);
+    }
+}
+
+// sign of (sum - v) for a double v > 0 with at most 18 significant bits on the grid
+// of unit 2^unit_exp; v's bits at or above the unit (the caller keeps them there)
+__host__ __device__ inline int cmp_sum(const Sum320 &a, double v, int unit_exp) {
+    int e;
+    const double f = frexp(v, &e);                       // v = f * 2^e, f in [0.5, 1)
+    const uint64_t mv = uint64_t(ldexp(f, 18));          // exact: v has <= 18 bits
+    const int sh = e - 18 - unit_exp;                    // v = mv * 2^sh units
+    if (sh > 320 - 18) return -1;                        // v >= 2^319 units: above any sum
+    // The midpoints compared lie within a few bf16 steps of sqrt(sum), whose square is at
+    // least the largest square (>= 2^(2F - 300) x 2^46 for a normal F, the whole grid
+    // below it being 2^(SQ_SHIFT - 46) units): their 18-bit squares sit far above the
+    // unit, so sh >= 0 for every comparison made.  A v off the grid (sh < 0) is compared
+    // by its integer part, ties above.
+    Sum320 b = {{0, 0, 0, 0, 0}, 0};
+    add_shifted(b, sh >= 0 ? mv : (mv >> (-sh < 63 ? -sh : 63)), (sh > 0 ? sh : 0));
+#pragma unroll
+    for (int i = 4; i >= 0; --i) {
+        if (a.l[i] != b.l[i]) return a.l[i] > b.l[i] ? 1 : -1;
+    }
+    return a.sticky ? 1 : (sh >= 0 ? 0 : -1);
+}
+
+// value of a non-negative bf16 pattern; the infinity stands for 2^128, so that its
+// midpoint with the largest finite value is the overflow threshold of rounding
+__host__ __device__ inline double bf16_pattern_value(uint32_t b) {
+    return b >= 0x7F80u ? ldexp(1.0, 128) : (double)__builtin_bit_cast(float, uint32_t(b << 16));
+}
+
+// bf16 nearest to sqrt(sum), ties to even: the answer is the bf16 value b whose
+// midpoints with its neighbours bracket sqrt(sum), decided by comparing the exact sum
+// with the midpoints' squares (9-bit midpoints: their squares are exact doubles)
+__host__ __device__ inline float bf16_sqrt_of_sum(const Sum320 &a, int unit_exp) {
+    int top = -1;
+#pragma unroll
+    for (int i = 4; i >= 0; --i)
+        if (top < 0 && a.l[i] != 0) top = i;
+    if (top < 0) return 0.0f;                            // every square is 0
+    double approx = ldexp((double)a.l[top], 64 * top + unit_exp);
+    if (top > 0) approx += ldexp((double)a.l[top - 1], 64 * (top - 1) + unit_exp);
+    uint32_t b = __builtin_bit_cast(uint32_t, bf16_from_double(sqrt(approx))) >> 16;
+    for (int it = 0; it < 8; ++it) {
+        const uint32_t hi = b >= 0x7F80u ? 0x7F80u : b + 1;
+        const double mhi = 0.5 * (bf16_pattern_value(b) + bf16_pattern_value(hi));
+        const double mlo = b == 0 ? 0.0 : 0.5 * (bf16_pattern_value(b - 1) + bf16_pattern_value(b));
+        const int c_hi = b >= 0x7F80u ? -1 : cmp_sum(a, mhi * mhi, unit_exp);
+        const int c_lo = b == 0 ? 1 : cmp_sum(a, mlo * mlo, unit_exp);
+        if (c_hi > 0 || (c_hi == 0 && (b & 1u))) b = hi;
+        else if (c_lo < 0 || (c_lo == 0 && (b & 1u))) b = b - 1;
+        else break;
+    }
+    return b >= 0x7F80u ? __builtin_bit_cast(float, 0x7F800000u) : __builtin_bit_cast(float, uint32_t(b << 16));
+}
+
+// One workgroup (256 threads) per row: the row's largest exponent, the exact sum of the
+// squares (per thread, then a fixed-order tree of exact additions), the norm, then the
+// indices of the element pairs.
 __global__ void __launch_bounds__(256) quant_cb4_kernel(const float *__restrict__ w, int K, float rk, Levels lv,
                                                         uint8_t *__restrict__ codes, uint16_t *__restrict__ norms) {
-    __shared__ double part[256];
+    __shared__ int fmax_part[256];
+    __shared__ Sum320 part[256];
     const int tid = threadIdx.x;
     const int64_t n = blockIdx.x;
     const float *wr = w + n * int64_t(K);
-    double ss = 0.0;
-    for (int k = tid; k < K; k += 256) {
-        const double x = (double)wr[k];
-        ss = fma(x, x, ss);                              // x*x is exact in float64
-    }
-    part[tid] = ss;
+    auto expo = [](uint32_t bits) { return max(int((bits >> 23) & 0xFFu), 1); };
+    int fm = 1;
+    for (int k = tid; k < K; k += 256) fm = max(fm, expo(__float_as_uint(wr[k])));
+    fmax_part[tid] = fm;
     __syncthreads();
     for (int s = 128; s >= 1; s >>= 1) {
-        if (tid < s) part[tid] += part[tid + s];
+        if (tid < s) fmax_part[tid] = max(fmax_part[tid], fmax_part[tid + s]);
         __syncthreads();
     }
-    const float nrm = bf16_from_double(sqrt(part[0]));
+    const int F = fmax_part[0];
+    Sum320 acc = {{0, 0, 0, 0, 0}, 0};
+    for (int k = tid; k < K; k += 256) {
+        const uint32_t bits = __float_as_uint(wr[k]) & 0x7FFFFFFFu;
+        const uint64_t m = (bits & 0x7FFFFFu) | (((bits >> 23) & 0xFFu) ? 0x800000u : 0u);
+        add_shifted(acc, m * m, 2 * (expo(bits) - F) + SQ_SHIFT);
+    }
+    part[tid] = acc;
+    __syncthreads();
+    for (int s = 128; s >= 1; s >>= 1) {
+        if (tid < s) {
+            Sum320 t = part[tid];
+            add320(t, part[tid + s]);
+            part[tid] = t;
+        }
+        __syncthreads();
+    }
+    const float nrm = bf16_sqrt_of_sum(part[0], 2 * F - 300 - SQ_SHIFT);
     const bool ok = nrm > 0.0f;
     for (int p = tid; p < K / 2; p += 256) {
         const float2 x = *reinterpret_cast<const float2 *>(wr + 2 * p);

@@ -144,3 +144,34 @@ def test_quantize_full_size_workload(name):
     assert torch.equal(scales.view(torch.uint8), s_ref.view(torch.uint8))
     if fmt == "int4" and not sym:
         assert torch.equal(aux.cpu(), torch.from_numpy(canon["zeros"]))
+
+
+def test_codebook_norm_exact_at_rounding_midpoints():
+    """Rows whose exact norm sits on, just above and just below a bf16 rounding midpoint
+    (where any float64 sum of the squares is ambiguous), rows spanning the float32
+    exponent range, the overflow and the all-zero row: the device norm is the oracle's
+    bf16 of the exact norm, bit for bit (both sum the squares exactly)."""
+    rng = np.random.default_rng(71)
+    K = 64
+    rows = []
+    for k in range(48):
+        mant = int(rng.integers(256, 512))
+        m = np.float32(np.ldexp(float(2 * mant + 1), int(rng.integers(-60, 60)) - 9))
+        r = np.zeros(K, np.float32)
+        r[int(rng.integers(0, K))] = m
+        if k % 3 == 1:
+            r[(int(rng.integers(0, K)) + 1) % K] = np.float32(np.ldexp(1.0, -50) * abs(float(m)))
+        if k % 3 == 2:
+            r[r != 0] = np.nextafter(m, np.float32(0))
+        rows.append(r)
+    for _ in range(16):
+        rows.append((rng.standard_normal(K) * 10.0 ** rng.uniform(-40, 37)).astype(np.float32))
+    rows.append(np.array([3e38] * 4 + [0] * (K - 4), np.float32))
+    rows.append(np.zeros(K, np.float32))
+    w = np.stack(rows)
+    canon = _oracle("cb4", w, 0, True)
+    codes, scales, _ = _device("cb4", w, 0, True)
+    torch.cuda.synchronize()
+    c_ref, s_ref, _ = to_device("cb4", canon)
+    assert torch.equal(scales.cpu().view(torch.uint8), s_ref.cpu().view(torch.uint8)), "norms"
+    assert torch.equal(codes.cpu(), c_ref.cpu()), "codes"
