@@ -34,7 +34,8 @@ of three timed replays):
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--sweep]
 Profiling helpers (used to write the summaries kept with the benchmark):
   python bench.py --probe decode|prefill   counter-collection workloads, no timing
-  python bench.py --summarize-trace D      per-kernel durations from a rocprofv3 CSV trace
+  python bench.py --summarize-trace D [--legs]  per-kernel durations from a rocprofv3 CSV
+                                           trace (--legs: per leg of a default run)
   python bench.py --summarize-pmc F W      decode traffic per forward from FETCH_SIZE /
                                            WRITE_SIZE runs of --probe decode
   python bench.py --summarize-prefill P T  matrix-core busy and clock per prefill leg from
@@ -211,6 +212,34 @@ def summarize_trace(d):
     return "\n".join(lines)
 
 
+def summarize_trace_legs(d):
+    """Per-leg kernel durations (µs) from a kernel trace of the default benchmark run,
+    split at its marker fills (one before each decode and prefill leg)."""
+    rows = _rows(os.path.join(d, "**", "*kernel_trace.csv"))
+    segs = _segments(rows)
+    labels = [lb for lb, _, _ in DECODE_LEGS] + [lb for lb, _, _ in PREFILL_LEGS]
+    if len(segs) < len(labels):
+        raise SystemExit(f"{len(segs)} segments, expected {len(labels)} legs")
+    lines = [f"{'leg':34s} {'calls':>6} {'avg_us':>9} {'median_us':>9} {'p95_us':>8} {'min_us':>8}  kernel"]
+    for label, seg in zip(labels, segs):
+        agg = {}
+        for g in seg:
+            name = g[0]["Kernel_Name"]
+            if any(k in name for k in FORWARD_KERNELS):
+                agg.setdefault(name, []).append((int(g[0]["End_Timestamp"]) - int(g[0]["Start_Timestamp"])) / 1e3)
+        for name, v in agg.items():
+            v = sorted(v)
+            p95 = v[min(len(v) - 1, int(np.ceil(0.95 * len(v))) - 1)]
+            lines.append(f"{label:34s} {len(v):6d} {sum(v) / len(v):9.3f} {v[len(v) // 2]:9.3f} {p95:8.3f} "
+                         f"{v[0]:8.3f}  {_short(name)}")
+    return "\n".join(lines)
+
+
+def _short(name):
+    """A kernel name without its argument list."""
+    return name.replace("(anonymous namespace)", "anon").split("(")[0]
+
+
 def _segments(rows, key=None):
     """Dispatch rows in dispatch order, split at the probe's marker fills (a torch fill of
     an int32 tensor between legs): [segment][rows]."""
@@ -271,7 +300,7 @@ def summarize_pmc(fetch_dir, write_dir):
         fb = f["kib"] * 1024 * res["fetch"]["factor"]
         wb = w["kib"] * 1024 * res["write"]["factor"]
         ab = leg_bytes(wl, M)
-        kern = ";".join(f"{k.split('(')[0]}x{n}" for k, n in f["kernels"].items())
+        kern = ";".join(f"{_short(k)} x{n}" for k, n in f["kernels"].items())
         lines.append(f"leg {label} fetch_bytes={fb:.0f} write_bytes={wb:.0f} traffic_bytes={fb + wb:.0f} "
                      f"alg_bytes={ab} ratio={(fb + wb) / ab:.4f}")
         lines.append(f"  kernels of {label}: {kern}")
@@ -306,11 +335,14 @@ def summarize_prefill(pmc_dir, trace_dir):
         us = durs[len(durs) // 2]
         cycles = med["GRBM_GUI_ACTIVE"] / XCDS
         busy = med["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / cycles
-        ghz = cycles / (us * 1e3)
-        lines.append(f"leg {label} mfma_busy={busy:.4f} clock_ghz={ghz:.3f} kernel_us={us:.3f} "
+        # engine clock: the GPU-busy cycles of the counter run over the kernel's traced
+        # duration (another run); the busy count also covers the dispatch around the
+        # kernel, so only kernels of 30 us and more give a usable figure
+        ghz = f" clock_ghz={cycles / (us * 1e3):.3f}" if us >= 30.0 else ""
+        lines.append(f"leg {label} mfma_busy={busy:.4f}{ghz} kernel_us={us:.3f} "
                      f"mfma_insts={med['SQ_INSTS_MFMA']:.0f} valu_per_mfma={(med['SQ_INSTS_VALU'] - med['SQ_INSTS_MFMA']) / med['SQ_INSTS_MFMA']:.3f} "
                      f"lds_insts={med['SQ_INSTS_LDS']:.0f} lds_bank_conflict_cycles={med['SQ_LDS_BANK_CONFLICT']:.0f}")
-        lines.append(f"  kernel of {label}: {main[0][0]['Kernel_Name']} ({len(main)} dispatches)")
+        lines.append(f"  kernel of {label}: {_short(main[0][0]['Kernel_Name'])} ({len(main)} dispatches)")
     lines.append(f"source_sha256: {kernel_source_hash()}")
     return "\n".join(lines)
 
@@ -322,7 +354,8 @@ class Flush:
 
     def __init__(self):
         import torch
-        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        # filled as bytes (a uint8 fill, not the int32 fill that marks legs in a trace)
+        self.buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda").view(torch.int32)
         self.sink = None
 
     def __call__(self):
@@ -497,11 +530,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=2.5, help="seconds per CPU-baseline run (3 runs per style)")
     ap.add_argument("--probe", choices=("decode", "prefill"))
     ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--legs", action="store_true", help="with --summarize-trace: per leg of the default line")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-prefill", nargs=2, metavar=("PMC_DIR", "TRACE_DIR"))
     args = ap.parse_args()
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace))
+        print(summarize_trace_legs(args.summarize_trace) if args.legs else summarize_trace(args.summarize_trace))
         return
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc))
@@ -525,6 +559,14 @@ def main():
     flush = Flush()
     traffic = recorded(TRAFFIC_FILE)
     pcount = recorded(PREFILL_COUNTERS_FILE)
+    # a marker fill before each leg, so that a kernel trace of this run splits per leg
+    # (bench.py --summarize-trace D --legs); outside every timed region
+    marker = torch.empty(1, dtype=torch.int32, device="cuda")
+    leg_no = [0]
+
+    def mark():
+        marker.fill_(leg_no[0])
+        leg_no[0] += 1
 
     # ---- decode legs; the step is the INT4 zero-point decode at M = 16 ----
     decode = {}
@@ -538,6 +580,7 @@ def main():
             pool, pool_name = _leg_pool(Q, wl, 7), wname
         x = torch.from_numpy(S.activations(wl, M)).cuda().to(torch.bfloat16)
         act = "swiglu" if wl.get("swiglu") else None
+        mark()
         if label == MAIN_LEG:
             # exactly --steps forwards per timed replay, one timed replay
             ms, _ = time_forward(Q, pool, x, act, args.steps, args.warmup, flush, use_graph, warm_s=AUX_WARM_S)
@@ -564,6 +607,7 @@ def main():
             torch.cuda.empty_cache()
             pool, pool_name = _leg_pool(Q, wl, 5), wname
         x = torch.from_numpy(S.activations(wl, M)).cuda().to(torch.bfloat16)
+        mark()
         ms, _ = time_forward(Q, pool, x, None, max(20, len(pool)), 3, flush, use_graph, warm_s=AUX_WARM_S, reps=3)
         fl = 2.0 * M * wl["N"] * wl["K"]
         tf = fl / (ms * 1e-3) / 1e12
@@ -574,6 +618,7 @@ def main():
                           "schedule": f"tile {sch.tile}, splits {sch.splits}"}
     pool = None
     torch.cuda.empty_cache()
+    mark()                                  # end of the legs of the line
 
     use_graph_sweep = use_graph
     others = {}

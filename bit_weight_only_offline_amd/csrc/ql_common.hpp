@@ -144,11 +144,11 @@ constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
 __host__ __device__ constexpr int cfg_rows(const TileCfg &t) { return 16 * t.MT * (t.kind == 2 ? t.WM : 1); }
 __host__ __device__ constexpr int cfg_ntiles(const TileCfg &t) { return t.kind == 0 ? t.NT : t.NT * t.WN; }
 // One stage of a decode wavefront's LDS ring: NT packed weight tiles, the chunk's
-// scale words and zero-point words (256-byte blocks), then the activation block: 16
-// rows x one chunk of bf16, or for batches that fit one activation load (xr = rows per
-// load, small batches) just that load's 1 KiB; with the fused SwiGLU input stage (sw,
-// always a one-load block), one more 1 KiB block for the gate rows (the up rows go to
-// the activation block, where h replaces them).
+// scale words and zero-point words (256-byte blocks), then the activation block of 16
+// rows x one chunk of bf16; with the fused SwiGLU input stage (sw) the batch's rows fit
+// one activation load, so the block is that load's 1 KiB, followed by one more 1 KiB
+// block for the gate rows (the up rows go to the activation block, where h replaces
+// them).
 __host__ __device__ constexpr int gemv_spc(int fmt, int gs) {
     return (fmt == FMT_INT4 || fmt == FMT_INT8) ? (gs <= chunk_k(fmt) / 32 ? chunk_k(fmt) / 32 / gs : 1) : 1;
 }
@@ -161,23 +161,19 @@ __host__ __device__ constexpr int gemv_zero_blocks(int fmt, bool zp, int gs, int
 }
 // activation rows of one 1 KiB load: 64 16-byte pieces, chunk_k(fmt) / 8 pieces a row
 __host__ __device__ constexpr int gemv_rows_per_load(int fmt) { return 64 / (chunk_k(fmt) / 8); }
-__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt, bool sw = false,
-                                                   bool small = false) {
+__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt, bool sw = false) {
     return nt * TILE_BYTES + 256 * (gemv_scale_blocks(fmt, gs, nt) + gemv_zero_blocks(fmt, zp, gs, nt)) +
-           ((small || sw) ? 1024 : 16 * chunk_k(fmt) * 2) + (sw ? 1024 : 0);
+           (sw ? 2048 : 16 * chunk_k(fmt) * 2);
 }
 constexpr int LDS_BYTES_MAX = 160 * 1024;
-// ring depth: PF stages per wavefront (one more for the one-load activation block, up
-// to 8), fewer if they would not fit the LDS
-__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false,
-                                                  bool small = false) {
-    return ((small || sw) && pf < 8 ? pf + 1 : pf) * wk * gemv_stage_bytes(fmt, zp, gs, nt, sw, small) <= LDS_BYTES_MAX
-               ? ((small || sw) && pf < 8 ? pf + 1 : pf)
-               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt, sw, small));
+// ring depth: PF stages per wavefront, fewer if they would not fit the LDS
+__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
+    return pf * wk * gemv_stage_bytes(fmt, zp, gs, nt, sw) <= LDS_BYTES_MAX
+               ? pf
+               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt, sw));
 }
-__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false,
-                                                 bool small = false) {
-    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf, sw, small) * gemv_stage_bytes(fmt, zp, gs, nt, sw, small);
+__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
+    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf, sw) * gemv_stage_bytes(fmt, zp, gs, nt, sw);
 }
 // LDS of a ring schedule: PF stages of activations + packed tiles + every wavefront's
 // scale and zero-point words, or, when WK > 1, the hand-over of one k-half's

@@ -15,17 +15,14 @@
 // the epilogue applies the codebook row scale and the bias and rounds to bf16.  No
 // workspace, no cross-workgroup traffic.
 //
-// Batches that fit one activation load (SMALL: up to 4 rows for the 4-bit formats, 8 for
-// INT8) hold only that load's 1 KiB per stage, which leaves room for one more stage in
-// flight; the A fragments of rows past the load read its rows again (rows at or beyond M
-// never reach a stored output).
-//
 // Fused SwiGLU input stage (SW, batches of at most SWIGLU_FUSE_MAX_M rows): the stage
 // receives the up rows in the activation block and the gate rows in one more block, and
 // the wavefront replaces each up value by h = bf16(up * silu(gate)) in LDS before it
 // reads its A fragments -- the same arithmetic as the prologue kernel that materialises
 // h for larger batches, so the two paths give the same linear.  Only the batch's rows
-// are evaluated, 64 lanes across one chunk of them.
+// are evaluated, 64 lanes across one chunk of them.  The stage then holds one activation
+// load (its rows fit it), and the A fragments of rows past that load read its rows again
+// (rows at or beyond M never reach a stored output).
 //
 // Codebook weights packed with the two-term operand (the record's split flag) issue a
 // second MFMA per k-step on the residual operand, so the product carries about 16
@@ -41,7 +38,7 @@
 
 namespace ql {
 
-template <int FMT, bool ZP, int GS, int NT, int WK, int PF, bool SW, bool SMALL>
+template <int FMT, bool ZP, int GS, int NT, int WK, int PF, bool SW>
 __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int CH = chunk_k(FMT);
     constexpr int STEPS = CH / 32;
@@ -53,11 +50,10 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int S_OFF = NT * TILE_BYTES;
     constexpr int Z_OFF = S_OFF + 256 * NSS;
     constexpr int X_OFF = Z_OFF + 256 * NSZ;
-    constexpr bool ONE = SW || SMALL;                 // a one-load activation block
-    constexpr int NI = ONE ? 1 : XB::NI;              // activation loads a stage holds
+    constexpr int NI = SW ? 1 : XB::NI;               // activation loads a stage holds
     constexpr int G_OFF = X_OFF + NI * 1024;          // gate rows (SW)
-    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT, SW, SMALL);
-    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF, SW, SMALL);
+    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT, SW);
+    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF, SW);
     static_assert(G_OFF + (SW ? 1024 : 0) == STAGE && S >= 1 && S <= 8, "stage layout");
     static_assert(gemv_rows_per_load(FMT) == XB::RPI, "rows per activation load");
     // fused SwiGLU: the batch's rows fit the first activation load; each lane forms HE
@@ -124,7 +120,7 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     uint32_t xfrag[STEPS];
 #pragma unroll
     for (int t = 0; t < STEPS; ++t)
-        xfrag[t] = uint32_t(X_OFF + XB::slot(ONE ? c % XB::RPI : c, 4 * t + g));
+        xfrag[t] = uint32_t(X_OFF + XB::slot(SW ? c % XB::RPI : c, 4 * t + g));
     // scale / zero-point words: word e of a chunk's scale block is word (e % 8) of the
     // record of tile e / (8 SPC), group slot (e / 8) % SPC (MXFP4: column e % 16 of tile
     // e / 16); zero-point words likewise with 2 words per record
