@@ -491,28 +491,53 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
         }
         return;
     }
+    // split-K partials: raw sums into the workspace (the reduction applies scale and bias)
+    if (a.ks != 1) {
 #pragma unroll
-    for (int mt = 0; mt < MTW; ++mt)
+        for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int n = (nt0 + wn * NTW + j) * TILE_N + c;
+            for (int j = 0; j < NTW; ++j) {
+                const int n = (nt0 + wn * NTW + j) * TILE_N + c;
+                if (n >= a.Np) continue;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + (wm * MTW + mt) * 16 + g * 4 + r;
-                if (m >= a.M) continue;
-                if (a.ks == 1) {
-                    if (n >= a.N) continue;
-                    // codebook row scale and bias: one fused multiply-add when both apply
-                    const float b = a.bias ? bf16_bits_to_f32(a.bias[n]) : 0.0f;
-                    const float v = FMT == FMT_CB4 ? (a.bias ? fmaf(acc[mt][j][r], rs[j], b) : acc[mt][j][r] * rs[j])
-                                                   : (a.bias ? acc[mt][j][r] + b : acc[mt][j][r]);
-                    if (a.out_f32) reinterpret_cast<float *>(a.out)[int64_t(m) * a.N + n] = v;
-                    else reinterpret_cast<__bf16 *>(a.out)[int64_t(m) * a.N + n] = (__bf16)v;
-                } else if (n < a.Np) {
-                    a.ws[(int64_t(kz) * a.M + m) * a.Np + n] = acc[mt][j][r];
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + (wm * MTW + mt) * 16 + g * 4 + r;
+                    if (m < a.M) a.ws[(int64_t(kz) * a.M + m) * a.Np + n] = acc[mt][j][r];
                 }
             }
-        }
+        return;
+    }
+    // an edge tile: per-element bounds, with the output type and the bias chosen once so
+    // that each unrolled element is one check and one store (a body small enough for the
+    // loops to unroll fully at every tile shape, which keeps acc in registers)
+    auto emit_edge = [&](auto f32c, auto biasc) {
+        constexpr bool F32 = decltype(f32c)::value, BIAS = decltype(biasc)::value;
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int n = (nt0 + wn * NTW + j) * TILE_N + c;
+                if (n >= a.N) continue;
+                // codebook row scale and bias: one fused multiply-add when both apply
+                const float b = BIAS ? bf16_bits_to_f32(a.bias[n]) : 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + (wm * MTW + mt) * 16 + g * 4 + r;
+                    if (m >= a.M) continue;
+                    const float v = FMT == FMT_CB4 ? (BIAS ? fmaf(acc[mt][j][r], rs[j], b) : acc[mt][j][r] * rs[j])
+                                                   : (BIAS ? acc[mt][j][r] + b : acc[mt][j][r]);
+                    if (F32) reinterpret_cast<float *>(a.out)[int64_t(m) * a.N + n] = v;
+                    else reinterpret_cast<__bf16 *>(a.out)[int64_t(m) * a.N + n] = (__bf16)v;
+                }
+            }
+    };
+    if (a.out_f32) {
+        if (a.bias) emit_edge(std::true_type{}, std::true_type{});
+        else emit_edge(std::true_type{}, std::false_type{});
+    } else {
+        if (a.bias) emit_edge(std::false_type{}, std::true_type{});
+        else emit_edge(std::false_type{}, std::false_type{});
+    }
 }
 
 }  // namespace ql
