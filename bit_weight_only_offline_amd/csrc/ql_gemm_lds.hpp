@@ -53,6 +53,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     static_assert(SPW * WKK == STEPS, "k-steps split evenly");
     constexpr bool INTF = (FMT == FMT_INT4 || FMT == FMT_INT8);
     constexpr int SPC = INTF ? (GS <= STEPS ? STEPS / GS : 1) : 1;
+    constexpr int SPCW = INTF ? (GS <= SPW ? SPW / GS : 1) : 1;   // groups per wavefront's steps
     constexpr int MP = 16 * MTW * WM;               // rows of the workgroup tile
     constexpr int NTT = NTW * WN;                   // column tiles of the workgroup
     constexpr int A_BYTES = MP * CH * 2;
@@ -258,7 +259,10 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
         const uint8_t *Bt = A + A_BYTES;
         const uint8_t *sc = A + A_BYTES + B_BYTES + wv * SCW;
         uint32_t wq[NTW][WPW];
-        uint32_t sq[NTW][SPC], zq[NTW][SPC];
+        // scale words of the groups this wavefront's k-steps fall in, indexed by the
+        // step's local group (a compile-time index: a run-time one would put the array
+        // in scratch memory)
+        uint32_t sq[NTW][SPCW], zq[NTW][SPCW];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const uint8_t *rec = Bt + (wn * NTW + j) * 1024 + lane * 16;
@@ -270,12 +274,15 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 wq[j][0] = v.x; wq[j][1] = v.y;
             }
 #pragma unroll
-            for (int q = 0; q < SPC; ++q) {
+            for (int q = 0; q < SPCW; ++q) {
                 if (FMT == FMT_MXFP4) {
                     sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + (j * 16 + c) * 4);
                 } else if (INTF) {
-                    sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + ((j * SPC + q) * 8 + (c >> 1)) * 4);
-                    if (ZP) zq[j][q] = *reinterpret_cast<const uint32_t *>(sc + NSS * 256 + ((j * SPC + q) * 2 + (c >> 3)) * 4);
+                    // the chunk's group slot: this wavefront's q-th group, or the one
+                    // group its steps lie in
+                    const int qg = GS > STEPS ? 0 : GS <= SPW ? kh * SPCW + q : (kh * SPW) / GS;
+                    sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + ((j * SPC + qg) * 8 + (c >> 1)) * 4);
+                    if (ZP) zq[j][q] = *reinterpret_cast<const uint32_t *>(sc + NSS * 256 + ((j * SPC + qg) * 2 + (c >> 3)) * 4);
                 }
             }
         }
@@ -327,10 +334,11 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 // fold the partial group sums at the last of this wavefront's steps in
                 // the group (a group may span both halves of a chunk, or several chunks)
                 bool boundary;
-                if (GS <= STEPS) boundary = ((t + 1) % GS) == 0 || tt == SPW - 1;
+                if (GS <= SPW) boundary = ((tt + 1) % GS) == 0;
+                else if (GS <= STEPS) boundary = tt == SPW - 1;
                 else boundary = (tt == SPW - 1) && (((kc + 1) % (GS / STEPS)) == 0);
                 if (boundary) {
-                    const int q = (GS <= STEPS) ? (t / GS) : 0;
+                    const int q = GS <= SPW ? tt / GS : 0;
 #pragma unroll
                     for (int j = 0; j < NTW; ++j) {
                         const uint32_t sbits = (sq[j][q] >> s_shift) & 0xFFFFu;

@@ -280,7 +280,10 @@ def test_zero_rows_is_noop_and_errors_leave_output():
     assert torch.all(out == 7.0)
 
 
-SCHED_CASES = [c for c in CASES if c[0] in ("int4_asym_g128", "int4_asym_g32", "int8_g256", "mxfp4", "cb4")]
+# every group slot layout: groups within a wavefront's k-steps (g32, g64), a group per
+# chunk (g128 INT4, g64 INT8) and groups spanning chunks (g256)
+SCHED_CASES = [c for c in CASES if c[0] in ("int4_asym_g128", "int4_asym_g32", "int4_sym_g64", "int8_g256",
+                                            "int8_g64", "int8_g32", "mxfp4", "cb4")]
 
 
 def _valid_schedules(Q, M):
