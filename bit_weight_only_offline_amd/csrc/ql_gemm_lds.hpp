@@ -127,10 +127,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     const int rot = (nck > 0) ? int(((int64_t(nblock % 16) * nck) / 16) / SPAN) * SPAN : 0;
     auto chunk_of = [&](int i) { return kc0 + (i + rot < nck ? i + rot : i + rot - nck); };
 
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint32_t(int64_t(a.M) * a.ldx * 2));
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.s, a.s_bytes);
-    const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z, ZP ? a.z_bytes : 0u);
+    const uint32_t x_bytes = uint32_t(int64_t(a.M) * a.ldx * 2);
     const uint32_t s_shift = 16u * (c & 1);
     const uint32_t z_shift = 8u * ((c >> 1) & 3) + 4u * (c & 1);
 
@@ -175,25 +172,29 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
 
     // scale / zero-point words: word e of this wavefront's scale block is word (e % 8) of
     // the record of its tile e / (8 SPC), group slot (e / 8) % SPC (MXFP4: column e % 16
-    // of tile e / 16); zero-point words likewise with 2 words per record
-    int s_tile[NSS > 0 ? NSS : 1], s_q[NSS > 0 ? NSS : 1], s_w[NSS > 0 ? NSS : 1];
+    // of tile e / 16); zero-point words likewise with 2 words per record.  The lane's
+    // offsets for chunk 0 (a later chunk moves the descriptor's base); words past this
+    // wavefront's records get bit 31: never fetched
+    uint32_t s_off[NSS > 0 ? NSS : 1], z_off[NSZ > 0 ? NSZ : 1];
 #pragma unroll
     for (int d = 0; d < NSS; ++d) {
         const int e = d * 64 + lane;
-        s_tile[d] = (FMT == FMT_MXFP4) ? e / 16 : e / (8 * SPC);
-        s_q[d] = (FMT == FMT_MXFP4) ? 0 : (e / 8) % SPC;
-        s_w[d] = (FMT == FMT_MXFP4) ? e % 16 : e % 8;
+        const int tile = (FMT == FMT_MXFP4) ? e / 16 : e / (8 * SPC);
+        const uint32_t ntg = uint32_t(nt0 + wn * NTW + tile);
+        if (FMT == FMT_MXFP4) s_off[d] = (ntg * uint32_t(a.kchunks) * TILE_N + uint32_t(e % 16)) * 4;
+        else s_off[d] = (ntg * uint32_t(a.ngroups) + uint32_t((e / 8) % SPC)) * (TILE_N * 2) + uint32_t(e % 8) * 4;
+        if (tile >= NTW) s_off[d] = 0x80000000u;
     }
-    int z_tile[NSZ > 0 ? NSZ : 1], z_q[NSZ > 0 ? NSZ : 1], z_w[NSZ > 0 ? NSZ : 1];
 #pragma unroll
     for (int d = 0; d < NSZ; ++d) {
         const int e = d * 64 + lane;
-        z_tile[d] = e / (2 * SPC);
-        z_q[d] = (e / 2) % SPC;
-        z_w[d] = e % 2;
+        const int tile = e / (2 * SPC);
+        z_off[d] = (uint32_t(nt0 + wn * NTW + tile) * uint32_t(a.ngroups) + uint32_t((e / 2) % SPC)) * 8 + uint32_t(e % 2) * 4;
+        if (tile >= NTW) z_off[d] = 0x80000000u;
     }
-    auto group_of = [&](int kc, int q) -> uint32_t {
-        return (GS <= STEPS) ? uint32_t(kc * (STEPS / GS) + q) : uint32_t(kc / (GS / STEPS));
+    // first group of chunk kc (INT4 / INT8)
+    auto group0 = [&](int kc) -> uint32_t {
+        return (GS <= STEPS) ? uint32_t(kc * (STEPS / GS)) : uint32_t(kc / (GS / STEPS));
     };
 
     // only the last chunk can reach past K: this lane's pieces of it that do are marked
@@ -206,54 +207,60 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     for (int q = 0; q < NAW; ++q)
         tail_mask[q] = ((a.kchunks - 1) * CH + a_k[q] >= a.K) ? 0x80000000u : 0u;
 
-    // issue the loads of chunk i (relative) into ring buffer buf
+    // issue the loads of chunk i (relative) into ring buffer buf.  The chunk's offsets go
+    // into the descriptors' base addresses (scalar arithmetic), so the lanes' offsets stay
+    // those of chunk 0 and a load takes no vector instruction
     auto issue = [&](int i, int buf) {
         const int kc = chunk_of(i);
         uint8_t *base = lds + buf * STAGE;
-        const uint32_t kbase2 = uint32_t(kc * CH) * 2u;
-        const uint32_t last = kc == a.kchunks - 1 ? 0xFFFFFFFFu : 0u;      // wave-uniform
+        const uint32_t xo = uint32_t(kc * CH) * 2u, wo = uint32_t(kc) * TILE_BYTES;
+        const __amdgpu_buffer_rsrc_t xc = make_rsrc(a.x + kc * CH, x_bytes - xo);
+        const __amdgpu_buffer_rsrc_t wc = make_rsrc(a.w + wo, a.w_bytes - wo);
+        if (kc == a.kchunks - 1) {
 #pragma unroll
-        for (int q = 0; q < NAW; ++q)
-            ld128_lds(xr, (a_off[q] + kbase2) | (tail_mask[q] & last), base + ((wv + W * q) % NA) * 1024);
+            for (int q = 0; q < NAW; ++q)
+                ld128_lds(xc, a_off[q] | tail_mask[q], base + ((wv + W * q) % NA) * 1024);
+        } else {
 #pragma unroll
-        for (int q = 0; q < NBW; ++q)
-            ld128_lds(wr, b_off[q] + uint32_t(kc) * TILE_BYTES, base + A_BYTES + ((wv + W * q) % NB) * 1024);
-        uint8_t *sc = base + A_BYTES + B_BYTES + wv * SCW;
-#pragma unroll
-        for (int d = 0; d < NSS; ++d) {
-            const uint32_t ntg = uint32_t(nt0 + wn * NTW + s_tile[d]);
-            uint32_t off;
-            if (FMT == FMT_MXFP4) off = ((ntg * uint32_t(a.kchunks) + uint32_t(kc)) * TILE_N + uint32_t(s_w[d])) * 4;
-            else off = (ntg * uint32_t(a.ngroups) + group_of(kc, s_q[d])) * (TILE_N * 2) + uint32_t(s_w[d]) * 4;
-            if (s_tile[d] >= NTW) off = 0x80000000u;               // past this wavefront's records
-            ld32_lds(sr, off, sc + d * 256);
+            for (int q = 0; q < NAW; ++q) ld128_lds(xc, a_off[q], base + ((wv + W * q) % NA) * 1024);
         }
 #pragma unroll
-        for (int d = 0; d < NSZ; ++d) {
-            const uint32_t ntg = uint32_t(nt0 + wn * NTW + z_tile[d]);
-            uint32_t off = (ntg * uint32_t(a.ngroups) + group_of(kc, z_q[d])) * 8 + uint32_t(z_w[d]) * 4;
-            if (z_tile[d] >= NTW) off = 0x80000000u;
-            ld32_lds(zr, off, sc + (NSS + d) * 256);
+        for (int q = 0; q < NBW; ++q) ld128_lds(wc, b_off[q], base + A_BYTES + ((wv + W * q) % NB) * 1024);
+        uint8_t *sc = base + A_BYTES + B_BYTES + wv * SCW;
+        if constexpr (NSS > 0) {
+            const uint32_t so = FMT == FMT_MXFP4 ? uint32_t(kc) * TILE_N * 4 : group0(kc) * (TILE_N * 2);
+            const __amdgpu_buffer_rsrc_t sc_r = make_rsrc(a.s + so, a.s_bytes - so);
+#pragma unroll
+            for (int d = 0; d < NSS; ++d) ld32_lds(sc_r, s_off[d], sc + d * 256);
+        }
+        if constexpr (NSZ > 0) {
+            const uint32_t zo = group0(kc) * 8;
+            const __amdgpu_buffer_rsrc_t zc_r = make_rsrc(a.z + zo, a.z_bytes - zo);
+#pragma unroll
+            for (int d = 0; d < NSZ; ++d) ld32_lds(zc_r, z_off[d], sc + (NSS + d) * 256);
         }
     };
 
     const u32x4 ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const bf16x8 ones = as_bf16x8(ones_u);
 
-    // this lane's A-fragment addresses inside a stage, for each of its k-steps of a chunk
-    uint32_t a_frag[SPW][MTW];
+    // this lane's A-fragment address inside a stage for each of its k-steps of a chunk,
+    // for the wavefront's first 16 rows: 16 rows further is one 16-row block further
+    // (the swizzle repeats every 16 rows), a constant the reads add as an immediate
+    using XB = XBlock<FMT>;
+    static_assert(XB::slot(16 + 5, 3) == XB::slot(5, 3) + XB::BYTES, "16-row blocks are contiguous");
+    uint32_t a_frag[SPW];
 #pragma unroll
     for (int tt = 0; tt < SPW; ++tt)
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
-            a_frag[tt][mt] = uint32_t(XBlock<FMT>::slot((wm * MTW + mt) * 16 + c, 4 * (kh * SPW + tt) + g));
+        a_frag[tt] = uint32_t(XB::slot(wm * MTW * 16 + c, 4 * (kh * SPW + tt) + g));
     // this wavefront's words of a lane's 16-byte weight record: all four, or with two
     // k-halves the two of its half (4-bit formats: one word per k-step; INT8: two)
     constexpr int WPW = 4 / WKK;
     static_assert(WKK == 1 || WKK == 2, "one or two k-halves");
 
-    auto compute = [&](int i, int buf, auto spl) {
-        constexpr bool SPLIT = decltype(spl)::value;
+    // INT4 / INT8: one chunk, k-step by k-step; each group's partial sums collect in
+    // tmp and are folded into acc with the group's scale (and offset) at the group's end
+    auto compute = [&](int i, int buf) {
         const int kc = chunk_of(i);
         const uint8_t *A = lds + buf * STAGE;
         const uint8_t *Bt = A + A_BYTES;
@@ -275,147 +282,208 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
             }
 #pragma unroll
             for (int q = 0; q < SPCW; ++q) {
-                if (FMT == FMT_MXFP4) {
-                    sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + (j * 16 + c) * 4);
-                } else if (INTF) {
-                    // the chunk's group slot: this wavefront's q-th group, or the one
-                    // group its steps lie in
-                    const int qg = GS > STEPS ? 0 : GS <= SPW ? kh * SPCW + q : (kh * SPW) / GS;
-                    sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + ((j * SPC + qg) * 8 + (c >> 1)) * 4);
-                    if (ZP) zq[j][q] = *reinterpret_cast<const uint32_t *>(sc + NSS * 256 + ((j * SPC + qg) * 2 + (c >> 3)) * 4);
-                }
+                // the chunk's group slot: this wavefront's q-th group, or the one group
+                // its steps lie in
+                const int qg = GS > STEPS ? 0 : GS <= SPW ? kh * SPCW + q : (kh * SPW) / GS;
+                sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + ((j * SPC + qg) * 8 + (c >> 1)) * 4);
+                if (ZP) zq[j][q] = *reinterpret_cast<const uint32_t *>(sc + NSS * 256 + ((j * SPC + qg) * 2 + (c >> 3)) * 4);
             }
-        }
-        // A fragments: with the codebook and MXFP4 (no group-sum registers) every k-step's
-        // fragments of the chunk are read up front, so the reads of the later k-steps are
-        // in flight during the MFMAs of the first; otherwise k-step by k-step
-        constexpr int AHOLD = INTF ? 1 : SPW;
-        bf16x8 afs[AHOLD][MTW];
-        if constexpr (AHOLD > 1) {
-#pragma unroll
-            for (int tt = 0; tt < SPW; ++tt)
-#pragma unroll
-                for (int mt = 0; mt < MTW; ++mt) afs[tt][mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt][mt]);
         }
 #pragma unroll
         for (int tt = 0; tt < SPW; ++tt) {
-            const int t = kh * SPW + tt;
-            bf16x8 *af = afs[AHOLD > 1 ? tt : 0];
-            if constexpr (AHOLD == 1) {
+            bf16x8 af[MTW];
 #pragma unroll
-                for (int mt = 0; mt < MTW; ++mt) af[mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt][mt]);
-            }
+            for (int mt = 0; mt < MTW; ++mt) af[mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt] + mt * XB::BYTES);
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
-                u32x4 bw;
-                if (FMT == FMT_INT4) bw = dec_int4(wq[j][tt]);
-                else if (FMT == FMT_INT8) bw = dec_int8<true>(wq[j][2 * tt], wq[j][2 * tt + 1]);
-                else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][tt], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
-                else {
-                    bw = dec_cb4(wq[j][tt], lut);
-                    if constexpr (SPLIT) {
-                        // the residual term first, then the leading term
-                        const bf16x8 bl = as_bf16x8(dec_cb4(wq[j][tt], lut2));
+                const bf16x8 bv = as_bf16x8(FMT == FMT_INT4 ? dec_int4(wq[j][tt])
+                                                            : dec_int8<true>(wq[j][2 * tt], wq[j][2 * tt + 1]));
 #pragma unroll
-                        for (int mt = 0; mt < MTW; ++mt) acc[mt][j] = mfma16x16x32(af[mt], bl, acc[mt][j]);
+                for (int mt = 0; mt < MTW; ++mt) tmp[mt][j] = mfma16x16x32(af[mt], bv, tmp[mt][j]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt)
+                if (FMT == FMT_INT4) xs[mt] = mfma16x16x32(af[mt], ones, xs[mt]);   // INT8 codes are signed
+            // fold the partial group sums at the last of this wavefront's steps in the
+            // group (a group may span both halves of a chunk, or several chunks)
+            bool boundary;
+            if (GS <= SPW) boundary = ((tt + 1) % GS) == 0;
+            else if (GS <= STEPS) boundary = tt == SPW - 1;
+            else boundary = (tt == SPW - 1) && (((kc + 1) % (GS / STEPS)) == 0);
+            if (boundary) {
+                const int q = GS <= SPW ? tt / GS : 0;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const uint32_t sbits = (sq[j][q] >> s_shift) & 0xFFFFu;
+                    float s, off;
+                    if (FMT == FMT_INT4) {
+                        s = f16_bits_to_f32(sbits);
+                        off = ZP ? 128.0f + float((zq[j][q] >> z_shift) & 0xFu) : 136.0f;
+                    } else {
+                        s = bf16_bits_to_f32(sbits);
+                        off = 0.0f;                   // the operand is the signed code
+                    }
+                    const float cz = -s * off;
+#pragma unroll
+                    for (int mt = 0; mt < MTW; ++mt) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            acc[mt][j][r] = fmaf(s, tmp[mt][j][r], acc[mt][j][r]);
+                            if (FMT == FMT_INT4) acc[mt][j][r] = fmaf(cz, xs[mt][r], acc[mt][j][r]);
+                        }
+                        tmp[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
                 }
-                const bf16x8 bv = as_bf16x8(bw);
 #pragma unroll
-                for (int mt = 0; mt < MTW; ++mt) {
-                    if (INTF) tmp[mt][j] = mfma16x16x32(af[mt], bv, tmp[mt][j]);
-                    else acc[mt][j] = mfma16x16x32(af[mt], bv, acc[mt][j]);
-                }
-            }
-            if (INTF) {
-#pragma unroll
-                for (int mt = 0; mt < MTW; ++mt)
-                    if (FMT == FMT_INT4) xs[mt] = mfma16x16x32(af[mt], ones, xs[mt]);   // INT8 codes are signed
-                // fold the partial group sums at the last of this wavefront's steps in
-                // the group (a group may span both halves of a chunk, or several chunks)
-                bool boundary;
-                if (GS <= SPW) boundary = ((tt + 1) % GS) == 0;
-                else if (GS <= STEPS) boundary = tt == SPW - 1;
-                else boundary = (tt == SPW - 1) && (((kc + 1) % (GS / STEPS)) == 0);
-                if (boundary) {
-                    const int q = GS <= SPW ? tt / GS : 0;
-#pragma unroll
-                    for (int j = 0; j < NTW; ++j) {
-                        const uint32_t sbits = (sq[j][q] >> s_shift) & 0xFFFFu;
-                        float s, off;
-                        if (FMT == FMT_INT4) {
-                            s = f16_bits_to_f32(sbits);
-                            off = ZP ? 128.0f + float((zq[j][q] >> z_shift) & 0xFu) : 136.0f;
-                        } else {
-                            s = bf16_bits_to_f32(sbits);
-                            off = 0.0f;                   // the operand is the signed code
-                        }
-                        const float cz = -s * off;
-#pragma unroll
-                        for (int mt = 0; mt < MTW; ++mt) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                acc[mt][j][r] = fmaf(s, tmp[mt][j][r], acc[mt][j][r]);
-                                if (FMT == FMT_INT4) acc[mt][j][r] = fmaf(cz, xs[mt][r], acc[mt][j][r]);
-                            }
-                            tmp[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        }
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < MTW; ++mt) xs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
-        }
-        if constexpr (!INTF) {
-            // Interleave the register decode with the MFMAs: the first tile's decode, then
-            // each MFMA followed by up to two VALU instructions, so that one wavefront
-            // keeps the matrix pipe fed while it decodes the next tile (left to itself
-            // the scheduler emits the MFMAs in bursts and the VALU work between them)
-            // The first k-step's A fragments are read up front; the later k-steps' reads
-            // are spread over the first k-step's MFMAs.
-            constexpr int NMF = SPW * NTW * MTW * (SPLIT ? 2 : 1);
-            constexpr int NRD = (SPW - 1) * MTW;             // fragment reads after the first k-step's
-            __builtin_amdgcn_sched_group_barrier(0x100, MTW + NTW, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
-#pragma unroll
-            for (int q = 0; q < NMF; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                for (int mt = 0; mt < MTW; ++mt) xs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
     };
 
-    // ---- prologue: stages 0 .. S-2 in flight ----
+    // wait until chunk i's loads (this wavefront's) have landed, given how many chunks'
+    // loads were issued after them
+    auto wait_later = [&](int later) {
+        if (later >= 6) wait_vmcnt<6 * PER_STAGE>();
+        else if (later == 5) wait_vmcnt<5 * PER_STAGE>();
+        else if (later == 4) wait_vmcnt<4 * PER_STAGE>();
+        else if (later == 3) wait_vmcnt<3 * PER_STAGE>();
+        else if (later == 2) wait_vmcnt<2 * PER_STAGE>();
+        else if (later == 1) wait_vmcnt<PER_STAGE>();
+        else wait_vmcnt<0>();
+    };
+    if constexpr (INTF) {
+        // ---- prologue: stages 0 .. S-2 in flight ----
 #pragma unroll
-    for (int u = 0; u < S - 1; ++u)
-        if (u < nck) issue(u, u);
+        for (int u = 0; u < S - 1; ++u)
+            if (u < nck) issue(u, u);
 
-    // ---- main loop, unrolled by the ring depth so ring slots are compile-time ----
-    auto main_loop = [&](auto spl) {
+        // ---- main loop, unrolled by the ring depth so ring slots are compile-time ----
         for (int i0 = 0; i0 < nck; i0 += S) {
 #pragma unroll
             for (int u = 0; u < S; ++u) {
                 const int i = i0 + u;
                 if (i < nck) {
                     // loads issued after chunk i's: those of chunks i+1 .. min(i+S-2, nck-1)
-                    const int later = min(S - 2, nck - 1 - i);
-                    if (later >= 6) wait_vmcnt<6 * PER_STAGE>();
-                    else if (later == 5) wait_vmcnt<5 * PER_STAGE>();
-                    else if (later == 4) wait_vmcnt<4 * PER_STAGE>();
-                    else if (later == 3) wait_vmcnt<3 * PER_STAGE>();
-                    else if (later == 2) wait_vmcnt<2 * PER_STAGE>();
-                    else if (later == 1) wait_vmcnt<PER_STAGE>();
-                    else wait_vmcnt<0>();
+                    wait_later(min(S - 2, nck - 1 - i));
                     ring_barrier();
                     if (i + S - 1 < nck) issue(i + S - 1, (u + S - 1) % S);
-                    compute(i, u, spl);
+                    compute(i, u);
                 }
             }
         }
-    };
-    if (FMT == FMT_CB4 && split) main_loop(std::true_type{});
-    else main_loop(std::false_type{});
+    } else {
+        // Codebook and MXFP4: pipelined over k-steps.  The A fragments of the next k-step
+        // are read during the MFMAs of the current one.  The ring barrier of chunk i+1
+        // comes before the last k-step of chunk i: by then every wavefront holds the rest
+        // of chunk i in registers, so chunk i's slot is refilled (with chunk i+S) at that
+        // barrier, and chunk i+1's weight words and first A fragments are read while the
+        // last MFMAs of chunk i run.  Chunk c lives in slot c % S.
+        static_assert(SPW >= 2 && SPW % 2 == 0, "fragment double buffer by k-step parity");
+        uint32_t wq[NTW][WPW], wqn[NTW][WPW], sw[NTW], swn[NTW];
+        bf16x8 af[2][MTW];
+        auto read_b = [&](int slot, uint32_t (&w)[NTW][WPW], uint32_t (&sx)[NTW]) {
+            const uint8_t *Bt = lds + slot * STAGE + A_BYTES;
+            const uint8_t *sc = Bt + B_BYTES + wv * SCW;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const uint8_t *rec = Bt + (wn * NTW + j) * 1024 + lane * 16;
+                if constexpr (WKK == 1) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(rec);
+                    w[j][0] = v.x; w[j][1] = v.y; w[j][2] = v.z; w[j][3] = v.w;
+                } else {
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(rec + kh * 8);
+                    w[j][0] = v.x; w[j][1] = v.y;
+                }
+                sx[j] = FMT == FMT_MXFP4 ? *reinterpret_cast<const uint32_t *>(sc + (j * 16 + c) * 4) : 0u;
+            }
+        };
+        auto read_a = [&](int slot, int tt, bf16x8 (&f)[MTW]) {
+            const uint8_t *A = lds + slot * STAGE;
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) f[mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt] + mt * XB::BYTES);
+        };
+        // one k-step's MFMAs, with the register decode of each weight fragment
+        // interleaved: the first fragment's decode, then each MFMA followed by up to two
+        // VALU instructions and one of the NRD fragment reads issued before it (left to
+        // itself the scheduler emits the MFMAs in bursts and the VALU work between them)
+        auto step = [&](const bf16x8 (&f)[MTW], const uint32_t (&w)[NTW][WPW], const uint32_t (&sx)[NTW], int tt,
+                        auto spl, auto nrdc) {
+            constexpr bool SPLIT = decltype(spl)::value;
+            constexpr int NRD = decltype(nrdc)::value;
+            const int t = kh * SPW + tt;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                u32x4 bw;
+                if (FMT == FMT_MXFP4) bw = dec_mxfp4(w[j][tt], e8m0_to_f32((sx[j] >> (8 * t)) & 0xFFu));
+                else {
+                    bw = dec_cb4(w[j][tt], lut);
+                    if constexpr (SPLIT) {
+                        // the residual term first, then the leading term
+                        const bf16x8 bl = as_bf16x8(dec_cb4(w[j][tt], lut2));
+#pragma unroll
+                        for (int mt = 0; mt < MTW; ++mt) acc[mt][j] = mfma16x16x32(f[mt], bl, acc[mt][j]);
+                    }
+                }
+                const bf16x8 bv = as_bf16x8(bw);
+#pragma unroll
+                for (int mt = 0; mt < MTW; ++mt) acc[mt][j] = mfma16x16x32(f[mt], bv, acc[mt][j]);
+            }
+            constexpr int NMF = NTW * MTW * (SPLIT ? 2 : 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, FMT == FMT_MXFP4 ? 8 : (SPLIT ? 28 : 14), 0);
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        };
+        using Mid = std::integral_constant<int, MTW>;
+        using Last = std::integral_constant<int, MTW + NTW * (FMT == FMT_MXFP4 ? 2 : 1)>;
+
+        // ---- prologue: chunks 0 .. S-2 in flight; chunk 0's words and first fragments ----
+#pragma unroll
+        for (int u = 0; u < S - 1; ++u)
+            if (u < nck) issue(u, u);
+        wait_later(min(S - 2, nck - 1));
+        ring_barrier();
+        if (S - 1 < nck) issue(S - 1, S - 1);
+        read_b(0, wq, sw);
+        read_a(0, 0, af[0]);
+
+        // ---- main loop, unrolled by the ring depth so ring slots are compile-time ----
+        auto main_loop = [&](auto spl) {
+            for (int i0 = 0; i0 < nck; i0 += S) {
+#pragma unroll
+                for (int u = 0; u < S; ++u) {
+                    const int i = i0 + u;
+                    if (i < nck) {
+#pragma unroll
+                        for (int tt = 0; tt < SPW - 1; ++tt) {
+                            read_a(u, tt + 1, af[(tt + 1) & 1]);
+                            step(af[tt & 1], wq, sw, tt, spl, Mid{});
+                        }
+                        // chunk i+1: loads issued after its own are those of chunks
+                        // i+2 .. min(i+S-1, nck-1); past the last chunk the reads below
+                        // fetch a stale slot, unused
+                        wait_later(min(S - 2, nck - 2 - i));
+                        ring_barrier();
+                        if (i + S < nck) issue(i + S, u);
+                        read_b((u + 1) % S, wqn, swn);
+                        read_a((u + 1) % S, 0, af[0]);
+                        step(af[1], wq, sw, SPW - 1, spl, Last{});
+#pragma unroll
+                        for (int j = 0; j < NTW; ++j) {
+                            sw[j] = swn[j];
+#pragma unroll
+                            for (int q = 0; q < WPW; ++q) wq[j][q] = wqn[j][q];
+                        }
+                    }
+                }
+            }
+        };
+        if (FMT == FMT_CB4 && split) main_loop(std::true_type{});
+        else main_loop(std::false_type{});
+    }
 
     if constexpr (WKK > 1) {
         // add the k-halves in a fixed order: the wavefronts of the second half hand their
