@@ -126,15 +126,17 @@ struct GemmArgs {
 //           and packed weights staged chunk by chunk into a PF-deep LDS ring by direct
 //           buffer->LDS loads (ql_gemm_lds.hpp); the input dimension may be split over
 //           workgroups (then a reduce kernel adds the partial sums in split order).
-// PF = weight chunks in flight per wavefront (kind 0) or ring depth (kind 2); SK is
-// unused (kept so every entry has the same fields).
-struct TileCfg { int kind, MT, NT, SK, PF, WK, WM, WN; };
+// PF = weight chunks in flight per wavefront (kind 0) or ring depth (kind 2); OCC (ring
+// schedules) = workgroups per compute unit that the kernel's registers and LDS must
+// allow, so that the wavefronts of two workgroups share each SIMD and one workgroup's
+// ring barrier does not idle the matrix cores (0: no bound beyond the workgroup size).
+struct TileCfg { int kind, MT, NT, OCC, PF, WK, WM, WN; };
 constexpr int NUM_TILE_CFGS = 22;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {0, 1, 1, 0, 4, 8, 1, 1}, {0, 1, 2, 0, 4, 8, 1, 1}, {0, 1, 4, 0, 4, 4, 1, 1}, {0, 1, 1, 0, 8, 4, 1, 1},
     {2, 2, 3, 0, 4, 2, 1, 2}, {2, 2, 2, 0, 4, 2, 1, 4}, {2, 4, 3, 0, 4, 2, 1, 2}, {2, 4, 2, 0, 4, 2, 1, 4},
     {2, 8, 3, 0, 3, 1, 1, 4}, {2, 8, 4, 0, 3, 1, 1, 4}, {2, 4, 4, 0, 3, 1, 2, 2}, {2, 4, 3, 0, 4, 1, 1, 4},
-    {2, 2, 4, 0, 4, 1, 1, 4}, {2, 8, 3, 0, 3, 2, 1, 4}, {2, 8, 4, 0, 3, 2, 1, 4}, {2, 4, 4, 0, 4, 2, 1, 4},
+    {2, 2, 4, 0, 4, 1, 1, 4}, {2, 8, 3, 0, 3, 2, 1, 4}, {2, 8, 3, 2, 2, 2, 1, 2}, {2, 4, 4, 0, 4, 2, 1, 4},
     {2, 4, 3, 0, 4, 2, 1, 4}, {2, 2, 4, 0, 6, 1, 1, 4}, {2, 4, 3, 0, 5, 1, 1, 4},
     {0, 1, 3, 0, 4, 4, 1, 1}, {0, 1, 7, 0, 3, 4, 1, 1},
     {2, 4, 4, 0, 2, 2, 1, 4},
@@ -196,6 +198,10 @@ __host__ __device__ constexpr int ring_lds_bytes(int fmt, bool zp, int gs, int w
                : wm * wn * mt * nt * 1024;
 }
 
+// OCC of a ring schedule where its LDS allows that many workgroups per compute unit,
+// else 0 (no register bound beyond the workgroup size)
+__host__ __device__ constexpr int ring_occ(int occ, int lds_bytes) { return occ * lds_bytes <= LDS_BYTES_MAX ? occ : 0; }
+
 struct Plan {
     int cfg = 0;          // index into TILE_CFGS
     int mtiles = 1, nblocks = 1, ks = 1, cps = 1;
@@ -212,14 +218,17 @@ constexpr int SWIGLU_FUSE_MAX_M = 2;
 inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 
 // Default schedule by batch size (measured on MI355X, weights read from HBM, over the
-// workload shapes and 3072^2 / 8192^2 / 28672 x 4096 weights of every format):
+// workload shapes and 3072^2 / 8192^2 / 28672 x 4096 / 4096 x 14336 weights):
 //   M <= 16      decode kernel, more column tiles per wavefront for wide layers;
 //   M <= 32      32 x 96 ring tiles (four wavefronts, two k-halves);
 //   M <= 64      64 x 128 ring tiles (eight wavefronts);
-//   then         weights that stay in the caches (under 16 MiB): 32 x 96 tiles up to
-//                M = 512; weights streamed from HBM: 64-row tiles with two k-halves up
-//                to M = 1024 (INT8: 64 x 256 with a four-deep ring, else 64 x 256 with a
-//                two-deep ring);
+//   codebook and MXFP4 weights streamed from HBM (16 MiB and more) with at least 192
+//                tiles of 128 x 256: those tiles, one wavefront per 128 x 64 (fewer
+//                activation re-reads per weight tile than the 64-row tiles);
+//   then         weights that stay in the caches: 32 x 96 tiles up to M = 512; 64-row
+//                tiles with two k-halves up to M = 1024 but for cache-resident INT8
+//                (INT8: 64 x 256 with a four-deep ring, else 64 x 256 with a two-deep
+//                ring);
 //   larger M     128 x 192 ring tiles, two wavefronts per tile (INT4: one wavefront per
 //                tile, whose group accumulators need the registers).
 // Split-K is added by make_plan when the tiles alone do not fill the machine.
@@ -246,8 +255,10 @@ inline int default_cfg(const Layout &L, int64_t M) {
     if (M <= 32) return 4;
     if (M <= 64) return 7;
     const bool streamed = L.w_bytes >= (size_t(16) << 20);
+    const bool lut4 = L.fmt == FMT_CB4 || L.fmt == FMT_MXFP4;
+    if (lut4 && streamed && ceil_div(M, int64_t(128)) * ceil_div(int64_t(L.ntiles), int64_t(16)) >= 192) return 9;
     if (!streamed && M <= 512) return 4;
-    if (streamed && M <= 1024) return L.fmt == FMT_INT8 ? 15 : 21;
+    if (M <= 1024 && (streamed || L.fmt != FMT_INT8)) return L.fmt == FMT_INT8 ? 15 : 21;
     if (L.fmt == FMT_INT8) return 13;
     return L.fmt == FMT_INT4 ? 8 : 13;
 }

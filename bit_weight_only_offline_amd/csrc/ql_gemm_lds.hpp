@@ -40,12 +40,22 @@ namespace ql {
 // the wavefront (vmcnt(0)): the stages issued ahead would be drained at each chunk.
 // Here each wavefront has already waited for exactly the loads the barrier publishes;
 // its own LDS reads are waited for (lgkmcnt(0)) so the buffer the barrier frees is no
-// longer being read, and the "memory" clobber keeps the compiler from moving LDS
-// accesses or loads across it.
-__device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// longer being read, and compiler fences keep LDS accesses and loads from moving across
+// it.  The wait and the barrier are builtins, not assembly text: the compiler's own
+// wait insertion then knows that every earlier LDS read has completed (after opaque
+// assembly it would wait again before the first use of each fragment read before the
+// barrier, counting the reads issued after it, and so stall the MFMAs on new reads).
+__device__ inline void ring_barrier() {
+    compiler_fence();
+    // gfx9 s_waitcnt: lgkmcnt (11:8) = 0; vmcnt (3:0, 15:14) and expcnt (6:4) at maxima
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
 
-template <int FMT, bool ZP, int GS, int WM, int WN, int WKK, int MTW, int NTW, int S>
-__global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs a) {
+template <int FMT, bool ZP, int GS, int WM, int WN, int WKK, int MTW, int NTW, int S, int OCC>
+__global__ void __launch_bounds__(64 * WM * WN * WKK)
+    __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC * WM * WN * WKK / 4 : 1))) qgemm_lds_kernel(GemmArgs a) {
     constexpr int W = WM * WN * WKK;
     constexpr int CH = chunk_k(FMT);
     constexpr int STEPS = CH / 32;
@@ -68,6 +78,8 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     constexpr int NB = NTT;                         // wave-wide B loads per stage
 
     static_assert(S >= 2 && S <= 8, "ring depth");
+    static_assert(OCC == 0 || OCC * ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S) <= LDS_BYTES_MAX,
+                  "the requested workgroups per compute unit fit in its LDS (ring_occ)");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
