@@ -121,6 +121,16 @@ struct XBlock {
 // Compiler-only fence: no memory access moves across it (the hardware is not waited).
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// Wait until this wavefront's LDS accesses have completed (lgkmcnt(0)), with compiler
+// fences on both sides.  A builtin, not assembly text, so that the compiler's own wait
+// insertion knows the reads are complete and adds no waits of its own for them later.
+__device__ inline void wait_lds() {
+    compiler_fence();
+    // gfx9 s_waitcnt: lgkmcnt (11:8) = 0; vmcnt (3:0, 15:14) and expcnt (6:4) at maxima
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    compiler_fence();
+}
+
 __device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ inline float f16_bits_to_f32(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);

@@ -46,9 +46,7 @@ namespace ql {
 // assembly it would wait again before the first use of each fragment read before the
 // barrier, counting the reads issued after it, and so stall the MFMAs on new reads).
 __device__ inline void ring_barrier() {
-    compiler_fence();
-    // gfx9 s_waitcnt: lgkmcnt (11:8) = 0; vmcnt (3:0, 15:14) and expcnt (6:4) at maxima
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wait_lds();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
 }

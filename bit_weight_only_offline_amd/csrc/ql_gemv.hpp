@@ -309,7 +309,7 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                     compute(i, u, spl);
                     if (i + S < nck) {
                         // the slot is refilled: this wavefront's accesses of it must be complete
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        wait_lds();
                         issue(i + S, u);
                     }
                 }
