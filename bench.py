@@ -40,6 +40,8 @@ Profiling helpers (used to write the summaries kept with the benchmark):
                                            WRITE_SIZE runs of --probe decode
   python bench.py --summarize-prefill P T  matrix-core busy and clock per prefill leg from
                                            a counter run and a trace run of --probe prefill
+  python bench.py --summarize-counters P.. any counters of the prefill legs' tile kernel
+                                           (stall, LDS, L2 and TA figures) from counter runs
 """
 from __future__ import annotations
 
@@ -64,6 +66,7 @@ POOL_BYTES = 1 << 30           # > 4 x the 256 MB Infinity Cache
 FLUSH_BYTES = 1 << 30          # read before every timed replay
 AUX_WARM_S = 0.25              # untimed replays before each timed leg
 COPY_BYTES = 256 << 20         # calibration copy for the traffic counters
+CUS = 256
 SIMDS = 1024                   # 256 compute units x 4
 XCDS = 8
 
@@ -347,6 +350,60 @@ def summarize_prefill(pmc_dir, trace_dir):
     return "\n".join(lines)
 
 
+
+def summarize_counters(*pmc_dirs):
+    """Where the tile kernel of each prefill leg spends its time, from counter runs of
+    `bench.py --probe prefill` (any counters, one or more runs): the median per dispatch of
+    every counter, and the fractions derived from those present.  SQ wave-cycle counters
+    count quad-cycles summed over waves; SIMD- and CU-cycle counters are per SIMD / CU."""
+    lines = []
+    med = {}
+    for d in pmc_dirs:
+        segs = _segments(_rows(os.path.join(d, "**", "*counter_collection.csv")))
+        if len(segs) != len(PREFILL_LEGS):
+            raise SystemExit(f"{d}: {len(segs)} segments, expected {len(PREFILL_LEGS)}")
+        for (label, _, _), seg in zip(PREFILL_LEGS, segs):
+            main = [g for g in seg if "qgemm_lds_kernel" in g[0]["Kernel_Name"]]
+            cnt = {}
+            for g in main:
+                per = {}
+                for r in g:
+                    per[r["Counter_Name"]] = per.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                for k, v in per.items():
+                    cnt.setdefault(k, []).append(v)
+            m = med.setdefault(label, {"kernel": _short(main[0][0]["Kernel_Name"]) if main else ""})
+            for k, v in cnt.items():
+                m[f"{k}@{os.path.basename(os.path.normpath(d))}"] = float(np.median(v))
+    for label, m in med.items():
+        lines.append(f"leg {label}: {m.pop('kernel')}")
+        def get(name):
+            vals = [v for k, v in m.items() if k.split("@")[0] == name]
+            return vals[0] if vals else None
+        for k in sorted(m):
+            lines.append(f"   {k:48s} {m[k]:16.1f}")
+        wave, cyc = get("SQ_WAVE_CYCLES"), get("GRBM_GUI_ACTIVE")
+        derived = []
+        if wave:
+            for name in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                         "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS"):
+                if get(name) is not None:
+                    derived.append(f"{name.lower()[3:]}/wave_cycles={get(name) / wave:.3f}")
+        if cyc:
+            c = cyc / XCDS
+            if get("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+                derived.append(f"mfma_busy={get('SQ_VALU_MFMA_BUSY_CYCLES') / SIMDS / c:.3f}")
+            if get("SQ_VALU_MFMA_COEXEC_CYCLES") is not None:
+                derived.append(f"valu_coexec_with_mfma={get('SQ_VALU_MFMA_COEXEC_CYCLES') / SIMDS / c:.3f}")
+            if get("SQ_LDS_IDX_ACTIVE") is not None:
+                derived.append(f"lds_busy={get('SQ_LDS_IDX_ACTIVE') / CUS / c:.3f}")
+            if get("TA_TA_BUSY") is not None:
+                derived.append(f"ta_busy={get('TA_TA_BUSY') / CUS / c:.3f}")
+        if get("TCC_HIT") is not None and get("TCC_MISS") is not None:
+            derived.append(f"l2_hit={get('TCC_HIT') / (get('TCC_HIT') + get('TCC_MISS')):.3f}")
+        lines.append("   derived: " + " ".join(derived))
+    lines.append(f"source_sha256: {kernel_source_hash()}")
+    return "\n".join(lines)
+
 class Flush:
     """Reads FLUSH_BYTES of device memory (four times the Infinity Cache), so that a
     following forward finds nothing of its working set cached.  Queued without a wait:
@@ -533,6 +590,7 @@ def main():
     ap.add_argument("--legs", action="store_true", help="with --summarize-trace: per leg of the default line")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-prefill", nargs=2, metavar=("PMC_DIR", "TRACE_DIR"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace_legs(args.summarize_trace) if args.legs else summarize_trace(args.summarize_trace))
@@ -542,6 +600,9 @@ def main():
         return
     if args.summarize_prefill:
         print(summarize_prefill(*args.summarize_prefill))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the library runs on one GPU (it has no multi-GPU path); use --gpus 1", file=sys.stderr)
