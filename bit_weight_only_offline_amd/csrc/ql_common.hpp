@@ -220,7 +220,7 @@ inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 // Default schedule by batch size (measured on MI355X, weights read from HBM, over the
 // workload shapes and 3072^2 / 8192^2 / 28672 x 4096 / 4096 x 14336 weights):
 //   M <= 16      decode kernel, more column tiles per wavefront for wide layers;
-//   M <= 32      32 x 96 ring tiles (four wavefronts, two k-halves);
+//   M <= 32      32 x 128 ring tiles (eight wavefronts, two k-halves);
 //   M <= 64      64 x 128 ring tiles (eight wavefronts);
 //   codebook and MXFP4 weights streamed from HBM (16 MiB and more) with at least 192
 //                tiles of 128 x 256: those tiles, one wavefront per 128 x 64 (fewer
@@ -252,7 +252,7 @@ inline int decode_cfg(int64_t ntiles) {
 
 inline int default_cfg(const Layout &L, int64_t M) {
     if (M <= 16) return decode_cfg(L.ntiles);
-    if (M <= 32) return 4;
+    if (M <= 32) return 5;
     if (M <= 64) return 7;
     const bool streamed = L.w_bytes >= (size_t(16) << 20);
     const bool lut4 = L.fmt == FMT_CB4 || L.fmt == FMT_MXFP4;
