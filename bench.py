@@ -187,7 +187,7 @@ def recorded(path):
     for ln in lines:
         if ln.startswith("leg "):
             parts = ln.split()
-            out[parts[1]] = {k: float(v) for k, v in (p.split("=", 1) for p in parts[2:])}
+            out[parts[1]] = {k: float(v) for k, v in (p.split("=", 1) for p in parts[2:] if "=" in p)}
     return out
 
 
@@ -375,7 +375,7 @@ def summarize_counters(*pmc_dirs):
             for k, v in cnt.items():
                 m[f"{k}@{os.path.basename(os.path.normpath(d))}"] = float(np.median(v))
     for label, m in med.items():
-        lines.append(f"leg {label}: {m.pop('kernel')}")
+        lines.append(f"tile kernel of {label}: {m.pop('kernel')}")
         def get(name):
             vals = [v for k, v in m.items() if k.split("@")[0] == name]
             return vals[0] if vals else None
