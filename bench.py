@@ -406,8 +406,11 @@ def summarize_counters(*pmc_dirs):
 
 class Flush:
     """Reads FLUSH_BYTES of device memory (four times the Infinity Cache), so that a
-    following forward finds nothing of its working set cached.  Queued without a wait:
-    the GPU is still busy with it while the host queues the timed work behind it."""
+    following forward finds nothing of its working set cached.  A max-reduction over
+    int32 reads the buffer and writes one value: a sum would first widen it to int64 (a
+    2 GiB write), and the caches would then hold dirty lines that the timed forwards
+    pay to write back.  Queued without a wait: the GPU is still busy with it while the
+    host queues the timed work behind it."""
 
     def __init__(self):
         import torch
@@ -416,7 +419,7 @@ class Flush:
         self.sink = None
 
     def __call__(self):
-        self.sink = self.buf.sum()
+        self.sink = self.buf.amax()
 
 
 def time_forward(Q, pool, x, act, steps, warmup, flush, use_graph=True, schedule=None, warm_s=0.0, reps=1):
