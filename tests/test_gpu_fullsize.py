@@ -27,10 +27,10 @@ TOL = 1e-2
 
 WORKLOADS = [
     ("int4_asym_decode", (1, 4, 8, 16)),
-    ("mxfp4_up", (1, 16, 64, 128, 512)),   # M = 128-512: the schedule of HBM-streamed weights
-    ("mxfp4_down", (1, 16, 64, 256)),
-    ("int8_swiglu", (1, 16, 128)),
-    ("cb4_prefill", (256, 2048)),
+    ("mxfp4_up", (1, 16, 64, 128, 512)),   # M = 128-512: the schedules of HBM-streamed weights
+    ("mxfp4_down", (1, 16, 32, 64, 256)),
+    ("int8_swiglu", (1, 16, 32, 128)),
+    ("cb4_prefill", (256, 1024, 2048)),
 ]
 
 _CACHE = {}
