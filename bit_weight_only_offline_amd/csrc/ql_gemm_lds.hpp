@@ -14,10 +14,13 @@
 //   B  the workgroup's packed 1 KiB weight tiles, copied verbatim (lane l's 16 bytes
 //      land at l*16, exactly where the lane that decodes them reads).
 // Per stage every wavefront waits for its own loads (s_waitcnt vmcnt), one barrier makes
-// all of them visible and frees the oldest buffer, the loads of the stage S-1 ahead are
-// issued, and the chunk is consumed: one read per packed tile (the lane's 16-byte record,
-// or with two k-halves the 8 bytes of its half), register decode, MTW x NTW MFMAs per
-// k-step.  Each wavefront's scale and zero-point words of the chunk
+// all of them visible and frees a buffer, the loads of a stage further ahead are issued,
+// and the chunk is consumed: one read per packed tile (the lane's 16-byte record, or
+// with two k-halves the 8 bytes of its half), register decode, MTW x NTW MFMAs per
+// k-step.  INT4 / INT8 take the chunks one after the other; the codebook and MXFP4 are
+// pipelined over k-steps (the next k-step's fragments are read during the current
+// k-step's MFMAs, and the next chunk's barrier comes before the current chunk's last
+// k-step).  Each wavefront's scale and zero-point words of the chunk
 // ride in the same stage (4-byte direct loads), so every load of the loop goes to LDS
 // and every wait is explicit.  Out-of-range
 // rows and inputs load as zero (ranged buffer loads).  Workgroups are numbered so that
@@ -43,8 +46,8 @@ namespace ql {
 // longer being read, and compiler fences keep LDS accesses and loads from moving across
 // it.  The wait and the barrier are builtins, not assembly text: the compiler's own
 // wait insertion then knows that every earlier LDS read has completed (after opaque
-// assembly it would wait again before the first use of each fragment read before the
-// barrier, counting the reads issued after it, and so stall the MFMAs on new reads).
+// assembly it waited again before the first use of each fragment read before the
+// barrier, counting the reads issued after it).
 __device__ inline void ring_barrier() {
     wait_lds();
     __builtin_amdgcn_s_barrier();

@@ -241,11 +241,12 @@ ql_status qlinear_workspace_bytes(ql_format f, int64_t M, int64_t N, int64_t K, 
  *   workspace  at least qlinear_workspace_bytes() bytes, 256-byte aligned (NULL if 0)
  * Schedules: for M <= 16 one workgroup per block of output columns streams the whole
  * input dimension, split over its wavefronts and reduced in LDS; larger M uses tiles of
- * 32 to 128 rows with activations staged through LDS, split over workgroups when the
- * column blocks alone do not fill the device.  The SwiGLU input is formed by a one-pass
- * prologue, or inside the decode kernel for M <= 2; both give the same h, so the fused
- * and the materialised paths give the same linear (piper-kernels, "ConvRot INT8").  Both accumulate in float32 and add
- * partial sums in a fixed order, so repeated calls give bit-identical results.
+ * 32 to 128 rows with activations and packed weights staged through LDS, split over
+ * workgroups when the column blocks alone do not fill the device.  Every schedule
+ * accumulates in float32 and adds partial sums in a fixed order, so repeated calls give
+ * bit-identical results.  The SwiGLU input is formed by a one-pass prologue, or inside
+ * the decode kernel for M <= 2; both give the same h, so the fused and the materialised
+ * paths give the same linear (piper-kernels, "ConvRot INT8").
  */
 ql_status qlinear_forward(const void *x, int64_t M, int64_t N, int64_t K,
                           const void *packed_w, const void *packed_s, const void *packed_aux,
