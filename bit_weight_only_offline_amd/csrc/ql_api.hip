@@ -287,7 +287,7 @@ GroupedPlan grouped_plan(int64_t T, int64_t E, int64_t N, int64_t K, ql_format f
     // (the decode kernel takes the slots as the grid's y dimension: past its limit the
     // 32-row ring tile, with the slots along x, serves instead)
     if (per <= 16 && ceil_div(T, 16) + E <= GRID_YZ_MAX) cfg = default_cfg(L, 16);   // decode, 16-row slots
-    else if (per <= 48) cfg = 5;                         // 32 x 128, two waves per tile
+    else if (per <= 48) cfg = (f == QL_INT4 || f == QL_INT8) ? 17 : 5;   // 32 x 128, two waves per tile
     else if (per <= 96) cfg = 16;                        // 64 x 192, two waves per tile
     else cfg = (f == QL_INT4 || f == QL_INT8) ? 8 : 13;  // 128 x 192
     g.plan = make_plan(L, 16, cfg, 1, PLAN_CUS, false);  // column blocks, chunks per wave

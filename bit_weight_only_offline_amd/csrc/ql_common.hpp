@@ -130,16 +130,20 @@ struct GemmArgs {
 // schedules) = workgroups per compute unit that the kernel's registers and LDS must
 // allow, so that the wavefronts of two workgroups share each SIMD and one workgroup's
 // ring barrier does not idle the matrix cores (0: no bound beyond the workgroup size).
-struct TileCfg { int kind, MT, NT, OCC, PF, WK, WM, WN; };
+// CP (ring schedules with WK = 2): the two wavefronts of a tile take alternate chunks,
+// each all of its chunk's k-steps, instead of alternate k-steps of every chunk; a ring
+// stage holds two chunks, so each workgroup walks half as many ring steps (and
+// barriers) in series.
+struct TileCfg { int kind, MT, NT, OCC, PF, WK, WM, WN, CP; };
 constexpr int NUM_TILE_CFGS = 22;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
-    {0, 1, 1, 0, 4, 8, 1, 1}, {0, 1, 2, 0, 4, 8, 1, 1}, {0, 1, 4, 0, 4, 4, 1, 1}, {0, 1, 1, 0, 8, 4, 1, 1},
-    {2, 2, 3, 0, 4, 2, 1, 2}, {2, 2, 2, 0, 4, 2, 1, 4}, {2, 4, 3, 0, 4, 2, 1, 2}, {2, 4, 2, 0, 4, 2, 1, 4},
-    {2, 8, 3, 0, 3, 1, 1, 4}, {2, 8, 4, 0, 3, 1, 1, 4}, {2, 4, 4, 0, 3, 1, 2, 2}, {2, 4, 3, 0, 4, 1, 1, 4},
-    {2, 2, 4, 0, 4, 1, 1, 4}, {2, 8, 3, 0, 3, 2, 1, 4}, {2, 8, 3, 2, 2, 2, 1, 2}, {2, 4, 4, 0, 4, 2, 1, 4},
-    {2, 4, 3, 0, 4, 2, 1, 4}, {2, 2, 4, 0, 6, 1, 1, 4}, {2, 4, 3, 0, 5, 1, 1, 4},
-    {0, 1, 3, 0, 4, 4, 1, 1}, {0, 1, 7, 0, 3, 4, 1, 1},
-    {2, 4, 4, 0, 2, 2, 1, 4},
+    {0, 1, 1, 0, 4, 8, 1, 1, 0}, {0, 1, 2, 0, 4, 8, 1, 1, 0}, {0, 1, 4, 0, 4, 4, 1, 1, 0}, {0, 1, 1, 0, 8, 4, 1, 1, 0},
+    {2, 2, 3, 0, 4, 2, 1, 2, 0}, {2, 2, 2, 0, 4, 2, 1, 4, 0}, {2, 4, 3, 0, 4, 2, 1, 2, 0}, {2, 4, 2, 0, 4, 2, 1, 4, 0},
+    {2, 8, 3, 0, 3, 1, 1, 4, 0}, {2, 8, 4, 0, 3, 1, 1, 4, 0}, {2, 4, 4, 0, 3, 1, 2, 2, 0}, {2, 4, 3, 0, 4, 1, 1, 4, 0},
+    {2, 2, 4, 0, 4, 1, 1, 4, 0}, {2, 8, 3, 0, 3, 2, 1, 4, 0}, {2, 4, 4, 0, 3, 2, 1, 4, 1}, {2, 4, 4, 0, 4, 2, 1, 4, 0},
+    {2, 4, 3, 0, 4, 2, 1, 4, 0}, {2, 2, 2, 0, 4, 2, 1, 4, 1}, {2, 4, 3, 0, 5, 1, 1, 4, 0},
+    {0, 1, 3, 0, 4, 4, 1, 1, 0}, {0, 1, 7, 0, 3, 4, 1, 1, 0},
+    {2, 4, 4, 0, 2, 2, 1, 4, 0},
 };
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.
@@ -184,17 +188,18 @@ __host__ __device__ constexpr int ring_stage_bytes(int fmt, bool zp, int gs, int
     return 16 * mt * wm * chunk_k(fmt) * 2 + nt * wn * TILE_BYTES +
            wm * wn * wk * 256 * (gemv_scale_blocks(fmt, gs, nt) + gemv_zero_blocks(fmt, zp, gs, nt));
 }
-// ring depth: PF stages, fewer if they would not fit the LDS
-__host__ __device__ constexpr int ring_depth(int fmt, bool zp, int gs, int wm, int wn, int wk, int mt, int nt, int pf) {
-    return pf * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt) <= LDS_BYTES_MAX
+// ring depth: PF stages of cs chunks, fewer if they would not fit the LDS
+__host__ __device__ constexpr int ring_depth(int fmt, bool zp, int gs, int wm, int wn, int wk, int mt, int nt, int pf,
+                                             int cs = 1) {
+    return pf * cs * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt) <= LDS_BYTES_MAX
                ? pf
-               : LDS_BYTES_MAX / ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt);
+               : LDS_BYTES_MAX / (cs * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt));
 }
 // pf: the ring depth actually used (ring_depth)
 __host__ __device__ constexpr int ring_lds_bytes(int fmt, bool zp, int gs, int wm, int wn, int wk, int mt, int nt,
-                                                 int pf) {
-    return pf * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt) > (wk > 1 ? wm * wn * mt * nt * 1024 : 0)
-               ? pf * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt)
+                                                 int pf, int cs = 1) {
+    return pf * cs * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt) > (wk > 1 ? wm * wn * mt * nt * 1024 : 0)
+               ? pf * cs * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt)
                : wm * wn * mt * nt * 1024;
 }
 
@@ -220,15 +225,16 @@ inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 // Default schedule by batch size (measured on MI355X, weights read from HBM, over the
 // workload shapes and 3072^2 / 8192^2 / 28672 x 4096 / 4096 x 14336 weights):
 //   M <= 16      decode kernel, more column tiles per wavefront for wide layers;
-//   M <= 32      32 x 128 ring tiles (eight wavefronts, two k-halves);
+//   M <= 32      32 x 128 ring tiles (eight wavefronts, two k-halves; INT4 / INT8 with
+//                the k-halves on alternate chunks);
 //   M <= 64      64 x 128 ring tiles (eight wavefronts);
 //   codebook and MXFP4 weights streamed from HBM (16 MiB and more) with at least 192
 //                tiles of 128 x 256: those tiles, one wavefront per 128 x 64 (fewer
 //                activation re-reads per weight tile than the 64-row tiles);
-//   then         weights that stay in the caches: 32 x 96 tiles up to M = 512; 64-row
-//                tiles with two k-halves up to M = 1024 but for cache-resident INT8
-//                (INT8: 64 x 256 with a four-deep ring, else 64 x 256 with a two-deep
-//                ring);
+//   then         weights that stay in the caches: 32 x 96 tiles up to M = 512; 64 x 256
+//                tiles with two k-halves up to M = 1024 but for cache-resident INT8 (INT4
+//                and INT8 streamed from HBM: the k-halves on alternate chunks, three
+//                stages of two chunks; else a two-deep ring);
 //   larger M     128 x 192 ring tiles, two wavefronts per tile (INT4: one wavefront per
 //                tile, whose group accumulators need the registers).
 // Split-K is added by make_plan when the tiles alone do not fill the machine.
@@ -251,14 +257,16 @@ inline int decode_cfg(int64_t ntiles) {
 }
 
 inline int default_cfg(const Layout &L, int64_t M) {
+    const bool intf = L.fmt == FMT_INT4 || L.fmt == FMT_INT8;
     if (M <= 16) return decode_cfg(L.ntiles);
-    if (M <= 32) return 5;
+    if (M <= 32) return intf ? 17 : 5;
     if (M <= 64) return 7;
     const bool streamed = L.w_bytes >= (size_t(16) << 20);
     const bool lut4 = L.fmt == FMT_CB4 || L.fmt == FMT_MXFP4;
     if (lut4 && streamed && ceil_div(M, int64_t(128)) * ceil_div(int64_t(L.ntiles), int64_t(16)) >= 192) return 9;
     if (!streamed && M <= 512) return 4;
-    if (M <= 1024 && (streamed || L.fmt != FMT_INT8)) return L.fmt == FMT_INT8 ? 15 : 21;
+    if (M <= 1024 && streamed && intf) return 14;
+    if (M <= 1024 && (streamed || L.fmt != FMT_INT8)) return 21;
     if (L.fmt == FMT_INT8) return 13;
     return L.fmt == FMT_INT4 ? 8 : 13;
 }

@@ -54,7 +54,7 @@ __device__ inline void ring_barrier() {
     compiler_fence();
 }
 
-template <int FMT, bool ZP, int GS, int WM, int WN, int WKK, int MTW, int NTW, int S, int OCC>
+template <int FMT, bool ZP, int GS, int WM, int WN, int WKK, int MTW, int NTW, int S, int OCC, bool CP>
 __global__ void __launch_bounds__(64 * WM * WN * WKK)
     __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC * WM * WN * WKK / 4 : 1))) qgemm_lds_kernel(GemmArgs a) {
     constexpr int W = WM * WN * WKK;
@@ -64,7 +64,11 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
     static_assert(SPW * WKK == STEPS, "k-steps split evenly");
     constexpr bool INTF = (FMT == FMT_INT4 || FMT == FMT_INT8);
     constexpr int SPC = INTF ? (GS <= STEPS ? STEPS / GS : 1) : 1;
-    constexpr int SPCW = INTF ? (GS <= SPW ? SPW / GS : 1) : 1;   // groups per wavefront's steps
+    // k-steps of a chunk one wavefront multiplies, its record words per lane, and the
+    // groups its k-steps fall in
+    constexpr int SPWC = CP ? STEPS : SPW;
+    constexpr int WPWC = CP ? 4 : 4 / WKK;
+    constexpr int SPCW = INTF ? (GS <= SPWC ? SPWC / GS : 1) : 1;
     constexpr int MP = 16 * MTW * WM;               // rows of the workgroup tile
     constexpr int NTT = NTW * WN;                   // column tiles of the workgroup
     constexpr int A_BYTES = MP * CH * 2;
@@ -79,7 +83,9 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
     constexpr int NB = NTT;                         // wave-wide B loads per stage
 
     static_assert(S >= 2 && S <= 8, "ring depth");
-    static_assert(OCC == 0 || OCC * ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S) <= LDS_BYTES_MAX,
+    static_assert(!CP || WKK == 2, "chunk-parallel k-halves: two wavefronts per tile");
+    constexpr int CS = CP ? 2 : 1;                  // chunks per ring stage
+    static_assert(OCC == 0 || OCC * ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S, CS) <= LDS_BYTES_MAX,
                   "the requested workgroups per compute unit fit in its LDS (ring_occ)");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -262,14 +268,31 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
     // (the swizzle repeats every 16 rows), a constant the reads add as an immediate
     using XB = XBlock<FMT>;
     static_assert(XB::slot(16 + 5, 3) == XB::slot(5, 3) + XB::BYTES, "16-row blocks are contiguous");
-    uint32_t a_frag[SPW];
+    uint32_t a_frag[SPWC];
 #pragma unroll
-    for (int tt = 0; tt < SPW; ++tt)
-        a_frag[tt] = uint32_t(XB::slot(wm * MTW * 16 + c, 4 * (kh * SPW + tt) + g));
-    // this wavefront's words of a lane's 16-byte weight record: all four, or with two
-    // k-halves the two of its half (4-bit formats: one word per k-step; INT8: two)
-    constexpr int WPW = 4 / WKK;
+    for (int tt = 0; tt < SPWC; ++tt)
+        a_frag[tt] = uint32_t(XB::slot(wm * MTW * 16 + c, 4 * ((CP ? 0 : kh * SPW) + tt) + g));
+    // this wavefront's words of a lane's 16-byte weight record (WPWC): all four, or with
+    // two k-halves splitting each chunk the two of its half (4-bit formats: one word per
+    // k-step; INT8: two)
     static_assert(WKK == 1 || WKK == 2, "one or two k-halves");
+
+    // ring steps: one chunk each, or with CP two (chunks 2r and 2r+1 of ring step r in
+    // chunk slots 2v and 2v+1 of ring slot v = r % S, one per k-half)
+    const int nrs = CP ? (nck + 1) / 2 : nck;
+    // chunks in ring steps a0 .. b0 (none when b0 < a0)
+    auto chunks_in = [&](int a0, int b0) {
+        return b0 < a0 ? 0 : CP ? min(2 * (b0 + 1), nck) - 2 * a0 : b0 - a0 + 1;
+    };
+    auto cslot = [&](int v) { return CP ? 2 * v + kh : v; };    // this wavefront's chunk slot
+    auto issue_rs = [&](int r, int v) {
+        if constexpr (CP) {
+            issue(2 * r, 2 * v);
+            if (2 * r + 1 < nck) issue(2 * r + 1, 2 * v + 1);
+        } else {
+            issue(r, v);
+        }
+    };
 
     // INT4 / INT8: one chunk, k-step by k-step; each group's partial sums collect in
     // tmp and are folded into acc with the group's scale (and offset) at the group's end
@@ -278,7 +301,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
         const uint8_t *A = lds + buf * STAGE;
         const uint8_t *Bt = A + A_BYTES;
         const uint8_t *sc = A + A_BYTES + B_BYTES + wv * SCW;
-        uint32_t wq[NTW][WPW];
+        uint32_t wq[NTW][WPWC];
         // scale words of the groups this wavefront's k-steps fall in, indexed by the
         // step's local group (a compile-time index: a run-time one would put the array
         // in scratch memory)
@@ -286,7 +309,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const uint8_t *rec = Bt + (wn * NTW + j) * 1024 + lane * 16;
-            if constexpr (WKK == 1) {
+            if constexpr (WPWC == 4) {
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(rec);
                 wq[j][0] = v.x; wq[j][1] = v.y; wq[j][2] = v.z; wq[j][3] = v.w;
             } else {
@@ -297,13 +320,14 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
             for (int q = 0; q < SPCW; ++q) {
                 // the chunk's group slot: this wavefront's q-th group, or the one group
                 // its steps lie in
-                const int qg = GS > STEPS ? 0 : GS <= SPW ? kh * SPCW + q : (kh * SPW) / GS;
+                const int kq = CP ? 0 : kh * SPW;          // first k-step of this wavefront
+                const int qg = GS > STEPS ? 0 : GS <= SPWC ? kq / GS + q : kq / GS;
                 sq[j][q] = *reinterpret_cast<const uint32_t *>(sc + ((j * SPC + qg) * 8 + (c >> 1)) * 4);
                 if (ZP) zq[j][q] = *reinterpret_cast<const uint32_t *>(sc + NSS * 256 + ((j * SPC + qg) * 2 + (c >> 3)) * 4);
             }
         }
 #pragma unroll
-        for (int tt = 0; tt < SPW; ++tt) {
+        for (int tt = 0; tt < SPWC; ++tt) {
             bf16x8 af[MTW];
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) af[mt] = *reinterpret_cast<const bf16x8 *>(A + a_frag[tt] + mt * XB::BYTES);
@@ -318,13 +342,16 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
             for (int mt = 0; mt < MTW; ++mt)
                 if (FMT == FMT_INT4) xs[mt] = mfma16x16x32(af[mt], ones, xs[mt]);   // INT8 codes are signed
             // fold the partial group sums at the last of this wavefront's steps in the
-            // group (a group may span both halves of a chunk, or several chunks)
+            // group (a group may span both halves of a chunk, or several chunks; with CP
+            // a wavefront sees every other chunk of a group, the last of them at chunk
+            // span-2 or span-1 of the group)
             bool boundary;
-            if (GS <= SPW) boundary = ((tt + 1) % GS) == 0;
-            else if (GS <= STEPS) boundary = tt == SPW - 1;
-            else boundary = (tt == SPW - 1) && (((kc + 1) % (GS / STEPS)) == 0);
+            if (GS <= SPWC) boundary = ((tt + 1) % GS) == 0;
+            else if (GS <= STEPS) boundary = tt == SPWC - 1;
+            else if (CP) boundary = (tt == SPWC - 1) && ((kc % (GS / STEPS)) >= GS / STEPS - 2);
+            else boundary = (tt == SPWC - 1) && (((kc + 1) % (GS / STEPS)) == 0);
             if (boundary) {
-                const int q = GS <= SPW ? tt / GS : 0;
+                const int q = GS <= SPWC ? tt / GS : 0;
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) {
                     const uint32_t sbits = (sq[j][q] >> s_shift) & 0xFFFFu;
@@ -365,42 +392,43 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
         else wait_vmcnt<0>();
     };
     if constexpr (INTF) {
-        // ---- prologue: stages 0 .. S-2 in flight ----
+        // ---- prologue: ring steps 0 .. S-2 in flight ----
 #pragma unroll
         for (int u = 0; u < S - 1; ++u)
-            if (u < nck) issue(u, u);
+            if (u < nrs) issue_rs(u, u);
 
         // ---- main loop, unrolled by the ring depth so ring slots are compile-time ----
-        for (int i0 = 0; i0 < nck; i0 += S) {
+        for (int r0 = 0; r0 < nrs; r0 += S) {
 #pragma unroll
             for (int u = 0; u < S; ++u) {
-                const int i = i0 + u;
-                if (i < nck) {
-                    // loads issued after chunk i's: those of chunks i+1 .. min(i+S-2, nck-1)
-                    wait_later(min(S - 2, nck - 1 - i));
+                const int r = r0 + u;
+                if (r < nrs) {
+                    // loads issued after step r's: those of steps r+1 .. min(r+S-2, nrs-1)
+                    wait_later(chunks_in(r + 1, min(r + S - 2, nrs - 1)));
                     ring_barrier();
-                    if (i + S - 1 < nck) issue(i + S - 1, (u + S - 1) % S);
-                    compute(i, u);
+                    if (r + S - 1 < nrs) issue_rs(r + S - 1, (u + S - 1) % S);
+                    if (!CP) compute(r, u);
+                    else if (2 * r + kh < nck) compute(2 * r + kh, cslot(u));
                 }
             }
         }
     } else {
         // Codebook and MXFP4: pipelined over k-steps.  The A fragments of the next k-step
-        // are read during the MFMAs of the current one.  The ring barrier of chunk i+1
-        // comes before the last k-step of chunk i: by then every wavefront holds the rest
-        // of chunk i in registers, so chunk i's slot is refilled (with chunk i+S) at that
-        // barrier, and chunk i+1's weight words and first A fragments are read while the
-        // last MFMAs of chunk i run.  Chunk c lives in slot c % S.
-        static_assert(SPW >= 2 && SPW % 2 == 0, "fragment double buffer by k-step parity");
-        uint32_t wq[NTW][WPW], wqn[NTW][WPW], sw[NTW], swn[NTW];
+        // are read during the MFMAs of the current one.  The ring barrier of step r+1
+        // comes before the last k-step of step r: by then every wavefront holds the rest
+        // of step r in registers, so its ring slot is refilled (with step r+S) at that
+        // barrier, and step r+1's weight words and first A fragments are read while the
+        // last MFMAs of step r run.
+        static_assert(SPWC >= 2 && SPWC % 2 == 0, "fragment double buffer by k-step parity");
+        uint32_t wq[NTW][WPWC], wqn[NTW][WPWC], sw[NTW], swn[NTW];
         bf16x8 af[2][MTW];
-        auto read_b = [&](int slot, uint32_t (&w)[NTW][WPW], uint32_t (&sx)[NTW]) {
+        auto read_b = [&](int slot, uint32_t (&w)[NTW][WPWC], uint32_t (&sx)[NTW]) {
             const uint8_t *Bt = lds + slot * STAGE + A_BYTES;
             const uint8_t *sc = Bt + B_BYTES + wv * SCW;
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const uint8_t *rec = Bt + (wn * NTW + j) * 1024 + lane * 16;
-                if constexpr (WKK == 1) {
+                if constexpr (WPWC == 4) {
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(rec);
                     w[j][0] = v.x; w[j][1] = v.y; w[j][2] = v.z; w[j][3] = v.w;
                 } else {
@@ -419,11 +447,11 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
         // interleaved: the first fragment's decode, then each MFMA followed by up to two
         // VALU instructions and one of the NRD fragment reads issued before it (left to
         // itself the scheduler emits the MFMAs in bursts and the VALU work between them)
-        auto step = [&](const bf16x8 (&f)[MTW], const uint32_t (&w)[NTW][WPW], const uint32_t (&sx)[NTW], int tt,
+        auto step = [&](const bf16x8 (&f)[MTW], const uint32_t (&w)[NTW][WPWC], const uint32_t (&sx)[NTW], int tt,
                         auto spl, auto nrdc) {
             constexpr bool SPLIT = decltype(spl)::value;
             constexpr int NRD = decltype(nrdc)::value;
-            const int t = kh * SPW + tt;
+            const int t = (CP ? 0 : kh * SPW) + tt;    // the k-step within the chunk
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 u32x4 bw;
@@ -453,42 +481,45 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
         using Mid = std::integral_constant<int, MTW>;
         using Last = std::integral_constant<int, MTW + NTW * (FMT == FMT_MXFP4 ? 2 : 1)>;
 
-        // ---- prologue: chunks 0 .. S-2 in flight; chunk 0's words and first fragments ----
+        // ---- prologue: ring steps 0 .. S-2 in flight; step 0's words and first fragments ----
 #pragma unroll
         for (int u = 0; u < S - 1; ++u)
-            if (u < nck) issue(u, u);
-        wait_later(min(S - 2, nck - 1));
+            if (u < nrs) issue_rs(u, u);
+        wait_later(chunks_in(1, min(S - 2, nrs - 1)));
         ring_barrier();
-        if (S - 1 < nck) issue(S - 1, S - 1);
-        read_b(0, wq, sw);
-        read_a(0, 0, af[0]);
+        if (S - 1 < nrs) issue_rs(S - 1, S - 1);
+        read_b(cslot(0), wq, sw);
+        read_a(cslot(0), 0, af[0]);
 
         // ---- main loop, unrolled by the ring depth so ring slots are compile-time ----
         auto main_loop = [&](auto spl) {
-            for (int i0 = 0; i0 < nck; i0 += S) {
+            for (int r0 = 0; r0 < nrs; r0 += S) {
 #pragma unroll
                 for (int u = 0; u < S; ++u) {
-                    const int i = i0 + u;
-                    if (i < nck) {
+                    const int r = r0 + u;
+                    if (r < nrs) {
+                        // with CP and an odd chunk count the last step has no chunk for
+                        // the second k-half (wave-uniform)
+                        const bool act = !CP || 2 * r + kh < nck;
 #pragma unroll
-                        for (int tt = 0; tt < SPW - 1; ++tt) {
-                            read_a(u, tt + 1, af[(tt + 1) & 1]);
-                            step(af[tt & 1], wq, sw, tt, spl, Mid{});
+                        for (int tt = 0; tt < SPWC - 1; ++tt) {
+                            read_a(cslot(u), tt + 1, af[(tt + 1) & 1]);
+                            if (act) step(af[tt & 1], wq, sw, tt, spl, Mid{});
                         }
-                        // chunk i+1: loads issued after its own are those of chunks
-                        // i+2 .. min(i+S-1, nck-1); past the last chunk the reads below
+                        // step r+1: loads issued after its own are those of steps
+                        // r+2 .. min(r+S-1, nrs-1); past the last step the reads below
                         // fetch a stale slot, unused
-                        wait_later(min(S - 2, nck - 2 - i));
+                        wait_later(chunks_in(r + 2, min(r + S - 1, nrs - 1)));
                         ring_barrier();
-                        if (i + S < nck) issue(i + S, u);
-                        read_b((u + 1) % S, wqn, swn);
-                        read_a((u + 1) % S, 0, af[0]);
-                        step(af[1], wq, sw, SPW - 1, spl, Last{});
+                        if (r + S < nrs) issue_rs(r + S, u);
+                        read_b(cslot((u + 1) % S), wqn, swn);
+                        read_a(cslot((u + 1) % S), 0, af[0]);
+                        if (act) step(af[1], wq, sw, SPWC - 1, spl, Last{});
 #pragma unroll
                         for (int j = 0; j < NTW; ++j) {
                             sw[j] = swn[j];
 #pragma unroll
-                            for (int q = 0; q < WPW; ++q) wq[j][q] = wqn[j][q];
+                            for (int q = 0; q < WPWC; ++q) wq[j][q] = wqn[j][q];
                         }
                     }
                 }
@@ -501,7 +532,7 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
     if constexpr (WKK > 1) {
         // add the k-halves in a fixed order: the wavefronts of the second half hand their
         // accumulators over through LDS (every ring is drained by now)
-        static_assert(WM * WN * MTW * NTW * 1024 <= ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S),
+        static_assert(WM * WN * MTW * NTW * 1024 <= ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S, CS),
                       "hand-over fits the allocation");
         __syncthreads();
         float *red = reinterpret_cast<float *>(lds);

@@ -40,7 +40,7 @@ def _grouped_schedule(Q, T, E, fmt, N, K, G):
     if per <= 16:
         return Q.default_schedule(fmt, 16, N, K, G).tile, 16
     if per <= 48:
-        return 5, 32
+        return (17 if fmt in ("int4", "int8") else 5), 32
     if per <= 96:
         return 16, 64
     return (8 if fmt in ("int4", "int8") else 13), 128
