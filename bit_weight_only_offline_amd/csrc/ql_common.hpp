@@ -126,24 +126,21 @@ struct GemmArgs {
 //           and packed weights staged chunk by chunk into a PF-deep LDS ring by direct
 //           buffer->LDS loads (ql_gemm_lds.hpp); the input dimension may be split over
 //           workgroups (then a reduce kernel adds the partial sums in split order).
-// PF = weight chunks in flight per wavefront (kind 0) or ring depth (kind 2); OCC (ring
-// schedules) = workgroups per compute unit that the kernel's registers and LDS must
-// allow, so that the wavefronts of two workgroups share each SIMD and one workgroup's
-// ring barrier does not idle the matrix cores (0: no bound beyond the workgroup size).
+// PF = weight chunks in flight per wavefront (kind 0) or ring depth (kind 2).
 // CP (ring schedules with WK = 2): the two wavefronts of a tile take alternate chunks,
 // each all of its chunk's k-steps, instead of alternate k-steps of every chunk; a ring
 // stage holds two chunks, so each workgroup walks half as many ring steps (and
 // barriers) in series.
-struct TileCfg { int kind, MT, NT, OCC, PF, WK, WM, WN, CP; };
+struct TileCfg { int kind, MT, NT, PF, WK, WM, WN, CP; };
 constexpr int NUM_TILE_CFGS = 22;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
-    {0, 1, 1, 0, 4, 8, 1, 1, 0}, {0, 1, 2, 0, 4, 8, 1, 1, 0}, {0, 1, 4, 0, 4, 4, 1, 1, 0}, {0, 1, 1, 0, 8, 4, 1, 1, 0},
-    {2, 2, 3, 0, 4, 2, 1, 2, 0}, {2, 2, 2, 0, 4, 2, 1, 4, 0}, {2, 4, 3, 0, 4, 2, 1, 2, 0}, {2, 4, 2, 0, 4, 2, 1, 4, 0},
-    {2, 8, 3, 0, 3, 1, 1, 4, 0}, {2, 8, 4, 0, 3, 1, 1, 4, 0}, {2, 4, 4, 0, 3, 1, 2, 2, 0}, {2, 4, 3, 0, 4, 1, 1, 4, 0},
-    {2, 2, 4, 0, 4, 1, 1, 4, 0}, {2, 8, 3, 0, 3, 2, 1, 4, 0}, {2, 4, 4, 0, 3, 2, 1, 4, 1}, {2, 4, 4, 0, 4, 2, 1, 4, 0},
-    {2, 4, 3, 0, 4, 2, 1, 4, 0}, {2, 2, 2, 0, 4, 2, 1, 4, 1}, {2, 4, 3, 0, 5, 1, 1, 4, 0},
-    {0, 1, 3, 0, 4, 4, 1, 1, 0}, {0, 1, 7, 0, 3, 4, 1, 1, 0},
-    {2, 4, 4, 0, 2, 2, 1, 4, 0},
+    {0, 1, 1, 4, 8, 1, 1, 0}, {0, 1, 2, 4, 8, 1, 1, 0}, {0, 1, 4, 4, 4, 1, 1, 0}, {0, 1, 1, 8, 4, 1, 1, 0},
+    {2, 2, 3, 4, 2, 1, 2, 0}, {2, 2, 2, 4, 2, 1, 4, 0}, {2, 4, 3, 4, 2, 1, 2, 0}, {2, 4, 2, 4, 2, 1, 4, 0},
+    {2, 8, 3, 3, 1, 1, 4, 0}, {2, 8, 4, 3, 1, 1, 4, 0}, {2, 4, 4, 3, 1, 2, 2, 0}, {2, 4, 3, 4, 1, 1, 4, 0},
+    {2, 2, 4, 4, 1, 1, 4, 0}, {2, 8, 3, 3, 2, 1, 4, 0}, {2, 4, 4, 3, 2, 1, 4, 1}, {2, 4, 4, 4, 2, 1, 4, 0},
+    {2, 4, 3, 4, 2, 1, 4, 0}, {2, 2, 2, 4, 2, 1, 4, 1}, {2, 4, 3, 5, 1, 1, 4, 0},
+    {0, 1, 3, 4, 4, 1, 1, 0}, {0, 1, 7, 3, 4, 1, 1, 0},
+    {2, 4, 4, 2, 2, 1, 4, 0},
 };
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.
@@ -202,10 +199,6 @@ __host__ __device__ constexpr int ring_lds_bytes(int fmt, bool zp, int gs, int w
                ? pf * cs * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt)
                : wm * wn * mt * nt * 1024;
 }
-
-// OCC of a ring schedule where its LDS allows that many workgroups per compute unit,
-// else 0 (no register bound beyond the workgroup size)
-__host__ __device__ constexpr int ring_occ(int occ, int lds_bytes) { return occ * lds_bytes <= LDS_BYTES_MAX ? occ : 0; }
 
 struct Plan {
     int cfg = 0;          // index into TILE_CFGS

@@ -54,9 +54,8 @@ __device__ inline void ring_barrier() {
     compiler_fence();
 }
 
-template <int FMT, bool ZP, int GS, int WM, int WN, int WKK, int MTW, int NTW, int S, int OCC, bool CP>
-__global__ void __launch_bounds__(64 * WM * WN * WKK)
-    __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC * WM * WN * WKK / 4 : 1))) qgemm_lds_kernel(GemmArgs a) {
+template <int FMT, bool ZP, int GS, int WM, int WN, int WKK, int MTW, int NTW, int S, bool CP>
+__global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs a) {
     constexpr int W = WM * WN * WKK;
     constexpr int CH = chunk_k(FMT);
     constexpr int STEPS = CH / 32;
@@ -85,8 +84,6 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK)
     static_assert(S >= 2 && S <= 8, "ring depth");
     static_assert(!CP || WKK == 2, "chunk-parallel k-halves: two wavefronts per tile");
     constexpr int CS = CP ? 2 : 1;                  // chunks per ring stage
-    static_assert(OCC == 0 || OCC * ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S, CS) <= LDS_BYTES_MAX,
-                  "the requested workgroups per compute unit fit in its LDS (ring_occ)");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
