@@ -35,7 +35,8 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
     } else {
         static_assert(t.kind == 2, "decode or LDS-ring schedule");
-        constexpr int cs = t.CP ? 2 : 1;          // chunks per ring stage
+        // chunks per ring stage: two for chunk-parallel schedules where two such stages fit
+        constexpr int cs = t.CP && 4 * ring_stage_bytes(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT) <= LDS_BYTES_MAX ? 2 : 1;
         constexpr int depth = ring_depth(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, t.PF, cs);
         constexpr size_t lds = ring_lds_bytes(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth, cs);
         auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth, t.CP != 0>;
