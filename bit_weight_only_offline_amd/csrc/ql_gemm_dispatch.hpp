@@ -39,7 +39,7 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
         constexpr int cs = t.CP && 4 * ring_stage_bytes(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT) <= LDS_BYTES_MAX ? 2 : 1;
         constexpr int depth = ring_depth(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, t.PF, cs);
         constexpr size_t lds = ring_lds_bytes(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth, cs);
-        auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth, t.CP != 0>;
+        auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth, cs == 2>;
         static_assert(lds <= LDS_BYTES_MAX, "ring fits the LDS");
         static bool attr_set = false;
         hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
