@@ -188,12 +188,21 @@ __device__ inline u32x4 dec_int4(uint32_t w) {
 // the offset 128 is then folded with the activation sum), both exact ----------------------
 template <bool SIGNED>
 __device__ inline u32x4 dec_int8(uint32_t d0, uint32_t d1) {
-    const float o = SIGNED ? 128.0f : 0.0f;
     u32x4 r;
-    r.x = pack_bf16x2((float)(d0 & 0xFFu) - o, (float)((d0 >> 8) & 0xFFu) - o);
-    r.y = pack_bf16x2((float)((d0 >> 16) & 0xFFu) - o, (float)(d0 >> 24) - o);
-    r.z = pack_bf16x2((float)(d1 & 0xFFu) - o, (float)((d1 >> 8) & 0xFFu) - o);
-    r.w = pack_bf16x2((float)((d1 >> 16) & 0xFFu) - o, (float)(d1 >> 24) - o);
+    if constexpr (SIGNED) {
+        // flipping bit 7 of every byte turns u into the two's-complement code q; a
+        // sign-extending byte select then converts it (one instruction per value)
+        const int32_t s0 = int32_t(d0 ^ 0x80808080u), s1 = int32_t(d1 ^ 0x80808080u);
+        r.x = pack_bf16x2((float)(int8_t)s0, (float)(int8_t)(s0 >> 8));
+        r.y = pack_bf16x2((float)(int8_t)(s0 >> 16), (float)(s0 >> 24));
+        r.z = pack_bf16x2((float)(int8_t)s1, (float)(int8_t)(s1 >> 8));
+        r.w = pack_bf16x2((float)(int8_t)(s1 >> 16), (float)(s1 >> 24));
+    } else {
+        r.x = pack_bf16x2((float)(d0 & 0xFFu), (float)((d0 >> 8) & 0xFFu));
+        r.y = pack_bf16x2((float)((d0 >> 16) & 0xFFu), (float)(d0 >> 24));
+        r.z = pack_bf16x2((float)(d1 & 0xFFu), (float)((d1 >> 8) & 0xFFu));
+        r.w = pack_bf16x2((float)((d1 >> 16) & 0xFFu), (float)(d1 >> 24));
+    }
     return r;
 }
 
