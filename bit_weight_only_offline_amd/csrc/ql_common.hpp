@@ -122,7 +122,9 @@ struct GemmArgs {
 //   kind 0 (decode, M <= 16): one workgroup per 16*NT output columns over the whole
 //           input dimension, split over WK wavefronts and reduced in LDS;
 //   kind 2 (LDS ring): WM x WN wavefronts, each 16*MT rows x 16*NT columns, times WK
-//           wavefronts that share a tile and split each chunk's k-steps; activations
+//           wavefronts that share a tile and split each chunk's k-steps (WK = 4 takes
+//           the four k-steps of a 4-bit chunk; INT8 chunks have two, so INT8 runs such
+//           a tile with WK = 2: the same tile and grid, half the wavefronts); activations
 //           and packed weights staged chunk by chunk into a PF-deep LDS ring by direct
 //           buffer->LDS loads (ql_gemm_lds.hpp); the input dimension may be split over
 //           workgroups (then a reduce kernel adds the partial sums in split order).
@@ -132,7 +134,7 @@ struct GemmArgs {
 // stage holds two chunks, so each workgroup walks half as many ring steps (and
 // barriers) in series.
 struct TileCfg { int kind, MT, NT, PF, WK, WM, WN, CP; };
-constexpr int NUM_TILE_CFGS = 22;
+constexpr int NUM_TILE_CFGS = 23;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {0, 1, 1, 4, 8, 1, 1, 0}, {0, 1, 2, 4, 8, 1, 1, 0}, {0, 1, 4, 4, 4, 1, 1, 0}, {0, 1, 1, 8, 4, 1, 1, 0},
     {2, 2, 3, 4, 2, 1, 2, 0}, {2, 2, 2, 4, 2, 1, 4, 0}, {2, 4, 3, 4, 2, 1, 2, 0}, {2, 4, 2, 4, 2, 1, 4, 0},
@@ -140,7 +142,7 @@ constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {2, 2, 4, 4, 1, 1, 4, 0}, {2, 8, 3, 3, 2, 1, 4, 0}, {2, 4, 4, 3, 2, 1, 4, 1}, {2, 4, 4, 4, 2, 1, 4, 0},
     {2, 4, 3, 4, 2, 1, 4, 0}, {2, 2, 2, 4, 2, 1, 4, 1}, {2, 4, 3, 5, 1, 1, 4, 0},
     {0, 1, 3, 4, 4, 1, 1, 0}, {0, 1, 7, 3, 4, 1, 1, 0},
-    {2, 4, 4, 2, 2, 1, 4, 0},
+    {2, 4, 4, 2, 2, 1, 4, 0}, {2, 2, 3, 4, 4, 1, 2, 0},
 };
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.
@@ -178,9 +180,12 @@ __host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int 
 __host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
     return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf, sw) * gemv_stage_bytes(fmt, zp, gs, nt, sw);
 }
+// k-parts a ring schedule runs with for a format: its WK where the chunk's k-steps
+// divide evenly, else 2
+__host__ __device__ constexpr int ring_wk(int fmt, int wk) { return (chunk_k(fmt) / 32) % wk == 0 ? wk : 2; }
 // LDS of a ring schedule: PF stages of activations + packed tiles + every wavefront's
-// scale and zero-point words, or, when WK > 1, the hand-over of one k-half's
-// accumulators if that is larger.
+// scale and zero-point words, or, when WK > 1, the hand-over of the accumulators of
+// the WK - 1 later k-parts if that is larger.
 __host__ __device__ constexpr int ring_stage_bytes(int fmt, bool zp, int gs, int wm, int wn, int wk, int mt, int nt) {
     return 16 * mt * wm * chunk_k(fmt) * 2 + nt * wn * TILE_BYTES +
            wm * wn * wk * 256 * (gemv_scale_blocks(fmt, gs, nt) + gemv_zero_blocks(fmt, zp, gs, nt));
@@ -195,9 +200,9 @@ __host__ __device__ constexpr int ring_depth(int fmt, bool zp, int gs, int wm, i
 // pf: the ring depth actually used (ring_depth)
 __host__ __device__ constexpr int ring_lds_bytes(int fmt, bool zp, int gs, int wm, int wn, int wk, int mt, int nt,
                                                  int pf, int cs = 1) {
-    return pf * cs * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt) > (wk > 1 ? wm * wn * mt * nt * 1024 : 0)
+    return pf * cs * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt) > (wk - 1) * wm * wn * mt * nt * 1024
                ? pf * cs * ring_stage_bytes(fmt, zp, gs, wm, wn, wk, mt, nt)
-               : wm * wn * mt * nt * 1024;
+               : (wk - 1) * wm * wn * mt * nt * 1024;
 }
 
 struct Plan {
@@ -224,7 +229,10 @@ inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 //   codebook and MXFP4 weights streamed from HBM (16 MiB and more) with at least 192
 //                tiles of 128 x 256: those tiles, one wavefront per 128 x 64 (fewer
 //                activation re-reads per weight tile than the 64-row tiles);
-//   then         weights that stay in the caches: 32 x 96 tiles up to M = 512; 64 x 256
+//   then         weights that stay in the caches: 32 x 96 tiles up to M = 512 (with four
+//                k-parts, eight wavefronts, where those tiles come to between three
+//                quarters of and one workgroup per CU: no split, and no second workgroup
+//                on a CU to hide the first one's waits); 64 x 256
 //                tiles with two k-halves up to M = 1024 but for cache-resident INT8 (INT4
 //                and INT8 streamed from HBM: the k-halves on alternate chunks, three
 //                stages of two chunks; else a two-deep ring);
@@ -257,7 +265,10 @@ inline int default_cfg(const Layout &L, int64_t M) {
     const bool streamed = L.w_bytes >= (size_t(16) << 20);
     const bool lut4 = L.fmt == FMT_CB4 || L.fmt == FMT_MXFP4;
     if (lut4 && streamed && ceil_div(M, int64_t(128)) * ceil_div(int64_t(L.ntiles), int64_t(16)) >= 192) return 9;
-    if (!streamed && M <= 512) return 4;
+    if (!streamed && M <= 512) {
+        const int64_t wgs = ceil_div(M, int64_t(32)) * ceil_div(int64_t(L.ntiles), int64_t(6));
+        return (4 * wgs >= 3 * 256 && wgs <= 256) ? 22 : 4;
+    }
     if (M <= 1024 && streamed && intf) return 14;
     if (M <= 1024 && (streamed || L.fmt != FMT_INT8)) return 21;
     if (L.fmt == FMT_INT8) return 13;

@@ -35,23 +35,24 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
     } else {
         static_assert(t.kind == 2, "decode or LDS-ring schedule");
+        constexpr int wk = ring_wk(FMT, t.WK);
         // chunks per ring stage: two for chunk-parallel schedules where two such stages fit
-        constexpr int cs = t.CP && 4 * ring_stage_bytes(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT) <= LDS_BYTES_MAX ? 2 : 1;
-        constexpr int depth = ring_depth(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, t.PF, cs);
-        constexpr size_t lds = ring_lds_bytes(FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth, cs);
-        auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, t.WK, t.MT, t.NT, depth, cs == 2>;
+        constexpr int cs = t.CP && 4 * ring_stage_bytes(FMT, ZP, GS, t.WM, t.WN, wk, t.MT, t.NT) <= LDS_BYTES_MAX ? 2 : 1;
+        constexpr int depth = ring_depth(FMT, ZP, GS, t.WM, t.WN, wk, t.MT, t.NT, t.PF, cs);
+        constexpr size_t lds = ring_lds_bytes(FMT, ZP, GS, t.WM, t.WN, wk, t.MT, t.NT, depth, cs);
+        auto kern = qgemm_lds_kernel<FMT, ZP, GS, t.WM, t.WN, wk, t.MT, t.NT, depth, cs == 2>;
         static_assert(lds <= LDS_BYTES_MAX, "ring fits the LDS");
         static bool attr_set = false;
         hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(p.mtiles * p.nblocks, p.ks), dim3(64 * t.WM * t.WN * t.WK), lds, st, a);
+        hipLaunchKernelGGL(kern, dim3(p.mtiles * p.nblocks, p.ks), dim3(64 * t.WM * t.WN * wk), lds, st, a);
     }
     return hipGetLastError();
 }
 
 template <int FMT, bool ZP, int GS>
 hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
-    static_assert(NUM_TILE_CFGS == 22, "one case per compiled schedule");
+    static_assert(NUM_TILE_CFGS == 23, "one case per compiled schedule");
     switch (p.cfg) {
         case 0: return launch_one<FMT, ZP, GS, 0>(p, a, st);
         case 1: return launch_one<FMT, ZP, GS, 1>(p, a, st);
@@ -75,6 +76,7 @@ hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
         case 19: return launch_one<FMT, ZP, GS, 19>(p, a, st);
         case 20: return launch_one<FMT, ZP, GS, 20>(p, a, st);
         case 21: return launch_one<FMT, ZP, GS, 21>(p, a, st);
+        case 22: return launch_one<FMT, ZP, GS, 22>(p, a, st);
         default: return hipErrorInvalidValue;
     }
 }

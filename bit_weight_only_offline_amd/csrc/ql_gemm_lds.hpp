@@ -3,10 +3,10 @@
 // lds), so nothing is staged through registers and several chunks are in flight.
 //
 // Workgroup = WM x WN x WKK wavefronts; a wavefront owns 16*MTW rows x 16*NTW columns, so
-// a workgroup covers 16*MTW*WM rows and 16*NTW*WN columns.  With WKK = 2 two wavefronts
-// share each output tile and take alternate halves of every chunk's k-steps (two
-// wavefronts per SIMD hide each other's LDS and decode latency); their accumulators are
-// added in LDS, in a fixed order, before the epilogue.  One ring stage holds one chunk
+// a workgroup covers 16*MTW*WM rows and 16*NTW*WN columns.  With WKK = 2 or 4, WKK
+// wavefronts share each output tile and each takes its share of every chunk's k-steps
+// (several wavefronts per SIMD hide each other's LDS and decode latency); their
+// accumulators are added in LDS, in a fixed order, before the epilogue.  One ring stage holds one chunk
 // of the input dimension (128 inputs, 64 for INT8):
 //   A  the tile's activation rows, loaded as whole row pieces of the chunk (full
 //      128-byte lines per load) and XOR-swizzled so that each lane's fragment is one
@@ -16,7 +16,7 @@
 // Per stage every wavefront waits for its own loads (s_waitcnt vmcnt), one barrier makes
 // all of them visible and frees a buffer, the loads of a stage further ahead are issued,
 // and the chunk is consumed: one read per packed tile (the lane's 16-byte record, or
-// with two k-halves the 8 bytes of its half), register decode, MTW x NTW MFMAs per
+// with WKK k-parts the words of its part), register decode, MTW x NTW MFMAs per
 // k-step.  INT4 / INT8 take the chunks one after the other; the codebook and MXFP4 are
 // pipelined over k-steps (the next k-step's fragments are read during the current
 // k-step's MFMAs, and the next chunk's barrier comes before the current chunk's last
@@ -270,9 +270,9 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     for (int tt = 0; tt < SPWC; ++tt)
         a_frag[tt] = uint32_t(XB::slot(wm * MTW * 16 + c, 4 * ((CP ? 0 : kh * SPW) + tt) + g));
     // this wavefront's words of a lane's 16-byte weight record (WPWC): all four, or with
-    // two k-halves splitting each chunk the two of its half (4-bit formats: one word per
-    // k-step; INT8: two)
-    static_assert(WKK == 1 || WKK == 2, "one or two k-halves");
+    // WKK k-parts splitting each chunk the 4 / WKK of its part (4-bit formats: one word
+    // per k-step; INT8: two)
+    static_assert(WKK == 1 || WKK == 2 || WKK == 4, "one, two or four k-parts");
 
     // ring steps: one chunk each, or with CP two (chunks 2r and 2r+1 of ring step r in
     // chunk slots 2v and 2v+1 of ring slot v = r % S, one per k-half)
@@ -309,9 +309,11 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
             if constexpr (WPWC == 4) {
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(rec);
                 wq[j][0] = v.x; wq[j][1] = v.y; wq[j][2] = v.z; wq[j][3] = v.w;
-            } else {
+            } else if constexpr (WPWC == 2) {
                 const u32x2 v = *reinterpret_cast<const u32x2 *>(rec + kh * 8);
                 wq[j][0] = v.x; wq[j][1] = v.y;
+            } else {
+                wq[j][0] = *reinterpret_cast<const uint32_t *>(rec + kh * 4);
             }
 #pragma unroll
             for (int q = 0; q < SPCW; ++q) {
@@ -416,7 +418,11 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
         // of step r in registers, so its ring slot is refilled (with step r+S) at that
         // barrier, and step r+1's weight words and first A fragments are read while the
         // last MFMAs of step r run.
-        static_assert(SPWC >= 2 && SPWC % 2 == 0, "fragment double buffer by k-step parity");
+        // fragment double buffer by k-step parity; with one k-step per wavefront the next
+        // step's fragments go to the other buffer and are moved over after the step
+        static_assert(SPWC == 1 || SPWC % 2 == 0, "fragment double buffer by k-step parity");
+        constexpr int CL = (SPWC - 1) & 1;      // buffer of a ring step's last k-step
+        constexpr int NX = SPWC == 1 ? 1 : 0;   // buffer the next ring step's first fragments go to
         uint32_t wq[NTW][WPWC], wqn[NTW][WPWC], sw[NTW], swn[NTW];
         bf16x8 af[2][MTW];
         auto read_b = [&](int slot, uint32_t (&w)[NTW][WPWC], uint32_t (&sx)[NTW]) {
@@ -428,9 +434,11 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                 if constexpr (WPWC == 4) {
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(rec);
                     w[j][0] = v.x; w[j][1] = v.y; w[j][2] = v.z; w[j][3] = v.w;
-                } else {
+                } else if constexpr (WPWC == 2) {
                     const u32x2 v = *reinterpret_cast<const u32x2 *>(rec + kh * 8);
                     w[j][0] = v.x; w[j][1] = v.y;
+                } else {
+                    w[j][0] = *reinterpret_cast<const uint32_t *>(rec + kh * 4);
                 }
                 sx[j] = FMT == FMT_MXFP4 ? *reinterpret_cast<const uint32_t *>(sc + (j * 16 + c) * 4) : 0u;
             }
@@ -510,8 +518,12 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
                         ring_barrier();
                         if (r + S < nrs) issue_rs(r + S, u);
                         read_b(cslot((u + 1) % S), wqn, swn);
-                        read_a(cslot((u + 1) % S), 0, af[0]);
-                        if (act) step(af[1], wq, sw, SPWC - 1, spl, Last{});
+                        read_a(cslot((u + 1) % S), 0, af[NX]);
+                        if (act) step(af[CL], wq, sw, SPWC - 1, spl, Last{});
+                        if constexpr (SPWC == 1) {
+#pragma unroll
+                            for (int mt = 0; mt < MTW; ++mt) af[0][mt] = af[1][mt];
+                        }
 #pragma unroll
                         for (int j = 0; j < NTW; ++j) {
                             sw[j] = swn[j];
@@ -527,29 +539,35 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     }
 
     if constexpr (WKK > 1) {
-        // add the k-halves in a fixed order: the wavefronts of the second half hand their
-        // accumulators over through LDS (every ring is drained by now)
-        static_assert(WM * WN * MTW * NTW * 1024 <= ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S, CS),
+        // add the k-parts in a fixed order, ((part 0 + part 1) + part 2) + part 3: the
+        // wavefronts of the later parts hand their accumulators over through LDS (every
+        // ring is drained by now)
+        constexpr int HB = WM * WN * MTW * NTW * 256;   // floats of one part's hand-over
+        static_assert((WKK - 1) * HB * 4 <= ring_lds_bytes(FMT, ZP, GS, WM, WN, WKK, MTW, NTW, S, CS),
                       "hand-over fits the allocation");
         __syncthreads();
         float *red = reinterpret_cast<float *>(lds);
         const int slot = wv % (WM * WN);
-        if (kh == 1) {
+        if (kh != 0) {
+            float *dst = red + (kh - 1) * HB;
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
                 for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) red[(((slot * MTW + mt) * NTW + j) * 4 + r) * 64 + lane] = acc[mt][j][r];
+                    for (int r = 0; r < 4; ++r) dst[(((slot * MTW + mt) * NTW + j) * 4 + r) * 64 + lane] = acc[mt][j][r];
         }
         __syncthreads();
         if (kh != 0) return;
 #pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
+        for (int p = 0; p < WKK - 1; ++p)
 #pragma unroll
-            for (int j = 0; j < NTW; ++j)
+            for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][j][r] += red[(((slot * MTW + mt) * NTW + j) * 4 + r) * 64 + lane];
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[mt][j][r] += red[p * HB + (((slot * MTW + mt) * NTW + j) * 4 + r) * 64 + lane];
     }
 
     // ---- epilogue ----
