@@ -380,9 +380,13 @@ __global__ void __launch_bounds__(64 * WM * WN * WKK) qgemm_lds_kernel(GemmArgs 
     };
 
     // wait until chunk i's loads (this wavefront's) have landed, given how many chunks'
-    // loads were issued after them
+    // loads were issued after them (at most 6 counted).  Away from the end of the input
+    // dimension that is every later ring step in flight, CS (S - 2) chunks: tested first,
+    // so the steady state takes one compare instead of the whole ladder
+    constexpr int STEADY = CS * (S - 2) < 6 ? CS * (S - 2) : 6;
     auto wait_later = [&](int later) {
-        if (later >= 6) wait_vmcnt<6 * PER_STAGE>();
+        if (later >= STEADY) wait_vmcnt<STEADY * PER_STAGE>();
+        else if (later >= 6) wait_vmcnt<6 * PER_STAGE>();
         else if (later == 5) wait_vmcnt<5 * PER_STAGE>();
         else if (later == 4) wait_vmcnt<4 * PER_STAGE>();
         else if (later == 3) wait_vmcnt<3 * PER_STAGE>();
