@@ -128,21 +128,27 @@ struct GemmArgs {
 //           and packed weights staged chunk by chunk into a PF-deep LDS ring by direct
 //           buffer->LDS loads (ql_gemm_lds.hpp); the input dimension may be split over
 //           workgroups (then a reduce kernel adds the partial sums in split order).
-// PF = weight chunks in flight per wavefront (kind 0) or ring depth (kind 2).
+// PF = weight chunks in flight per wavefront (kind 0) or ring depth (kind 2).  The
+// decode schedules keep two chunks in flight but one: a plain stream of HBM reads on
+// MI355X is fastest with about 8 KiB outstanding per wavefront and slows with more (a
+// 58.7 MB read at 16 or 24 KiB per wavefront took 9-25% longer), and the decode rings
+// measured the same way (two-deep against three- and four-deep: 3-8% faster at the
+// 4096 x 4096 INT4, 4096 x 14336 MXFP4 and 8192 x 28672 INT8 workloads).
 // CP (ring schedules with WK = 2): the two wavefronts of a tile take alternate chunks,
 // each all of its chunk's k-steps, instead of alternate k-steps of every chunk; a ring
 // stage holds two chunks, so each workgroup walks half as many ring steps (and
 // barriers) in series.
 struct TileCfg { int kind, MT, NT, PF, WK, WM, WN, CP; };
-constexpr int NUM_TILE_CFGS = 23;
+constexpr int NUM_TILE_CFGS = 24;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
-    {0, 1, 1, 4, 8, 1, 1, 0}, {0, 1, 2, 4, 8, 1, 1, 0}, {0, 1, 4, 4, 4, 1, 1, 0}, {0, 1, 1, 8, 4, 1, 1, 0},
+    {0, 1, 1, 2, 8, 1, 1, 0}, {0, 1, 2, 2, 8, 1, 1, 0}, {0, 1, 4, 2, 4, 1, 1, 0}, {0, 1, 1, 8, 4, 1, 1, 0},
     {2, 2, 3, 4, 2, 1, 2, 0}, {2, 2, 2, 4, 2, 1, 4, 0}, {2, 4, 3, 4, 2, 1, 2, 0}, {2, 4, 2, 4, 2, 1, 4, 0},
     {2, 8, 3, 3, 1, 1, 4, 0}, {2, 8, 4, 3, 1, 1, 4, 0}, {2, 4, 4, 3, 1, 2, 2, 0}, {2, 4, 3, 4, 1, 1, 4, 0},
     {2, 2, 4, 4, 1, 1, 4, 0}, {2, 8, 3, 3, 2, 1, 4, 0}, {2, 4, 4, 3, 2, 1, 4, 1}, {2, 4, 4, 4, 2, 1, 4, 0},
     {2, 4, 3, 4, 2, 1, 4, 0}, {2, 2, 2, 4, 2, 1, 4, 1}, {2, 4, 3, 5, 1, 1, 4, 0},
-    {0, 1, 3, 4, 4, 1, 1, 0}, {0, 1, 7, 3, 4, 1, 1, 0},
+    {0, 1, 3, 2, 4, 1, 1, 0}, {0, 1, 7, 2, 4, 1, 1, 0},
     {2, 4, 4, 2, 2, 1, 4, 0}, {2, 2, 3, 4, 4, 1, 2, 0},
+    {0, 1, 1, 4, 8, 1, 1, 0},
 };
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.
@@ -242,7 +248,13 @@ inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 // Decode schedule: the one whose busiest compute unit streams the fewest column tiles,
 // counting one resident workgroup per CU (256 CUs), ties to the wider schedule (fewer
 // rounds of workgroups).  Candidates in order of columns per workgroup: 1, 2, 3, 4, 7.
-inline int decode_cfg(int64_t ntiles) {
+// One column tile per workgroup over a long input dimension (each of the eight
+// wavefronts walking 12 chunks or more) at up to 4 rows (one activation load per chunk)
+// keeps four chunks in flight instead of two, since such a chunk is a small load
+// (measured at 4096 x 14336: 8.9 against 9.3 us at M = 1; at M = 16, with four
+// activation loads per chunk, and at 4096 x 4096, four chunks per wavefront, two-deep
+// is as fast or faster).
+inline int decode_cfg(int64_t ntiles, int64_t kchunks, int64_t M) {
     constexpr int cands[] = {0, 1, 19, 2, 20};
     int best = 0;
     int64_t best_load = -1;
@@ -254,12 +266,13 @@ inline int decode_cfg(int64_t ntiles) {
             best_load = load;
         }
     }
+    if (best == 0 && M <= 4 && ceil_div(kchunks, int64_t(TILE_CFGS[0].WK)) >= 12) best = 23;
     return best;
 }
 
 inline int default_cfg(const Layout &L, int64_t M) {
     const bool intf = L.fmt == FMT_INT4 || L.fmt == FMT_INT8;
-    if (M <= 16) return decode_cfg(L.ntiles);
+    if (M <= 16) return decode_cfg(L.ntiles, L.kchunks, M);
     if (M <= 32) return intf ? 17 : 5;
     if (M <= 64) return 7;
     const bool streamed = L.w_bytes >= (size_t(16) << 20);
