@@ -225,6 +225,34 @@ def test_schedule_entry_points(L):
     assert L.qlinear_workspace_bytes_ex(INT4, 8, 4096, 4096, 128, 0, ctypes.byref(dec2), ctypes.byref(b)) == 4
 
 
+def test_decode_schedule_choice(L):
+    """Decode schedules (M <= 16): the column tiles per workgroup follow the busiest
+    compute unit's load (256 CUs), and a single-tile workgroup over a long input
+    dimension (eight wavefronts of 12 chunks or more) at up to 4 rows takes the
+    four-deep ring instead of the two-deep one (same tile shape, another schedule)."""
+    import bit_weight_only_offline_amd as Q
+    r, c, k = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+
+    def pick(fmt, M, N, K, G, act=0):
+        s = Q.Schedule()
+        assert L.qlinear_default_schedule(fmt, M, N, K, G, act, ctypes.byref(s)) == QL_OK
+        assert L.qlinear_tile_shape(s.tile, ctypes.byref(r), ctypes.byref(c), ctypes.byref(k)) == QL_OK
+        assert k.value == 0 and s.splits == 1            # the decode kernel: no split, no staging
+        return s.tile, (r.value, c.value)
+
+    # 4096 x 4096 INT4: one column tile per workgroup, four chunks per wavefront -> two-deep at every M
+    t4 = {M: pick(INT4, M, 4096, 4096, 128) for M in (1, 4, 8, 16)}
+    assert len({t for t, _ in t4.values()}) == 1 and t4[1][1] == (16, 16)
+    # 4096 x 14336 MXFP4: 14 chunks per wavefront -> the four-deep schedule at M <= 4 only
+    d1, d4, d16 = (pick(MXFP4, M, 4096, 14336, 32) for M in (1, 4, 16))
+    assert d1 == d4 and d1[1] == d16[1] == (16, 16) and d1[0] != d16[0]
+    assert d16[0] == t4[16][0]
+    # 28672 x 4096 MXFP4 gate/up: 1792 column tiles -> seven per workgroup (256 workgroups)
+    assert pick(MXFP4, 1, 28672, 4096, 32)[1] == (16, 112)
+    # 8192 x 28672 INT8 with the SwiGLU input: 512 column tiles -> two per workgroup
+    assert pick(INT8, 1, 8192, 28672, 256, 1)[1] == (16, 32)
+
+
 def test_launch_grid_limits(L):
     """Schedules whose launch grid exceeds the device's limits (65535 along the second
     and third grid dimensions, 2^31 - 1 along the first) are refused before any launch."""
