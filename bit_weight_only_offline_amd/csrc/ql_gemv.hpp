@@ -3,7 +3,8 @@
 // One workgroup owns NT column tiles (16*NT output columns) over the whole input
 // dimension; its WK wavefronts split the chunks of the input dimension into WK
 // contiguous runs (whole groups each).  Every wavefront streams its run through a
-// private LDS ring, several chunks ahead, with direct buffer->LDS loads only: per chunk
+// private LDS ring, as many chunks ahead as the schedule's ring depth (two, or four for
+// one column tile over a long input dimension), with direct buffer->LDS loads only: per chunk
 // the packed weight tiles, the scale and zero-point words and the activation block
 // (16 rows x one chunk of inputs).  The activation loads read whole rows of the chunk
 // (full 128-byte lines) and only the rows below M are requested; a XOR swizzle of the
