@@ -139,7 +139,7 @@ struct GemmArgs {
 // stage holds two chunks, so each workgroup walks half as many ring steps (and
 // barriers) in series.
 struct TileCfg { int kind, MT, NT, PF, WK, WM, WN, CP; };
-constexpr int NUM_TILE_CFGS = 24;
+constexpr int NUM_TILE_CFGS = 25;
 constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {0, 1, 1, 2, 8, 1, 1, 0}, {0, 1, 2, 2, 8, 1, 1, 0}, {0, 1, 4, 2, 4, 1, 1, 0}, {0, 1, 1, 8, 4, 1, 1, 0},
     {2, 2, 3, 4, 2, 1, 2, 0}, {2, 2, 2, 4, 2, 1, 4, 0}, {2, 4, 3, 4, 2, 1, 2, 0}, {2, 4, 2, 4, 2, 1, 4, 0},
@@ -148,7 +148,7 @@ constexpr TileCfg TILE_CFGS[NUM_TILE_CFGS] = {
     {2, 4, 3, 4, 2, 1, 4, 0}, {2, 2, 2, 4, 2, 1, 4, 1}, {2, 4, 3, 5, 1, 1, 4, 0},
     {0, 1, 3, 2, 4, 1, 1, 0}, {0, 1, 7, 2, 4, 1, 1, 0},
     {2, 4, 4, 2, 2, 1, 4, 0}, {2, 2, 3, 4, 4, 1, 2, 0},
-    {0, 1, 1, 4, 8, 1, 1, 0},
+    {0, 1, 1, 4, 8, 1, 1, 0}, {0, 1, 1, 2, 4, 1, 1, 0},
 };
 
 // Rows / columns of output covered by one workgroup of a tile or LDS-ring schedule.

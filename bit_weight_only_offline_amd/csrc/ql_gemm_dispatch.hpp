@@ -52,7 +52,7 @@ hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
 
 template <int FMT, bool ZP, int GS>
 hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
-    static_assert(NUM_TILE_CFGS == 24, "one case per compiled schedule");
+    static_assert(NUM_TILE_CFGS == 25, "one case per compiled schedule");
     switch (p.cfg) {
         case 0: return launch_one<FMT, ZP, GS, 0>(p, a, st);
         case 1: return launch_one<FMT, ZP, GS, 1>(p, a, st);
@@ -78,6 +78,7 @@ hipError_t launch_qmm_cfg(const Plan &p, const GemmArgs &a, hipStream_t st) {
         case 21: return launch_one<FMT, ZP, GS, 21>(p, a, st);
         case 22: return launch_one<FMT, ZP, GS, 22>(p, a, st);
         case 23: return launch_one<FMT, ZP, GS, 23>(p, a, st);
+        case 24: return launch_one<FMT, ZP, GS, 24>(p, a, st);
         default: return hipErrorInvalidValue;
     }
 }

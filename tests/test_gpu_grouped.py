@@ -35,10 +35,13 @@ def _experts(fmt, G, sym, E, N, K, seed):
 
 def _grouped_schedule(Q, T, E, fmt, N, K, G):
     """(tile, rows per slot) the library plans for a grouped call: the decode kernel in
-    slots of 16 rows when experts average at most 16 tokens, else ring tiles."""
+    slots of 16 rows when experts average at most 16 tokens (its four-wavefront
+    single-tile schedule, 24, where the dense default is the eight-wavefront one, 0),
+    else ring tiles."""
     per = (T + E - 1) // E
     if per <= 16:
-        return Q.default_schedule(fmt, 16, N, K, G).tile, 16
+        tile = Q.default_schedule(fmt, 16, N, K, G).tile
+        return (24 if tile == 0 else tile), 16
     if per <= 48:
         return (17 if fmt in ("int4", "int8") else 5), 32
     if per <= 96:
