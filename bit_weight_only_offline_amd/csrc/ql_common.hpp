@@ -129,7 +129,8 @@ struct GemmArgs {
 //           buffer->LDS loads (ql_gemm_lds.hpp); the input dimension may be split over
 //           workgroups (then a reduce kernel adds the partial sums in split order).
 // PF = weight chunks in flight per wavefront (kind 0) or ring depth (kind 2).  The
-// decode schedules keep two chunks in flight but one: a plain stream of HBM reads on
+// decode schedules keep two chunks in flight, but for two single-tile ones (four and
+// eight chunks, for small chunks over a long input dimension): a plain stream of HBM reads on
 // MI355X is fastest with about 8 KiB outstanding per wavefront and slows with more (a
 // 58.7 MB read at 16 or 24 KiB per wavefront took 9-25% longer), and the decode rings
 // measured the same way (two-deep against three- and four-deep: 3-8% faster at the
