@@ -211,6 +211,13 @@ __device__ inline u32x4 dec_int8(uint32_t d0, uint32_t d1) {
 __device__ inline float e8m0_to_f32(uint32_t e) {
     return __uint_as_float(e ? (e << 23) | (((e + 1u) >> 8) << 22) : 0x00400000u);
 }
+// Codes 1..254 are the float32 exponent field itself: 2^(e-127) has the bits e << 23.
+__device__ inline float e8m0_to_f32_normal(uint32_t e) { return __uint_as_float(e << 23); }
+// Nonzero when any byte of the word is code 0 or 255, the two codes e << 23 does not give
+// (the high bit of a zero byte of w or of ~w survives the borrow test).
+__device__ inline uint32_t e8m0_special_bytes(uint32_t w) {
+    return (((w - 0x01010101u) & ~w) | ((~w - 0x01010101u) & w)) & 0x80808080u;
+}
 
 __device__ inline u32x4 dec_mxfp4(uint32_t w, float scale) {
     u32x4 r;

@@ -247,6 +247,18 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                 }
             }
         }
+        // MXFP4: when no scale code of the chunk's words is 0 or 255 anywhere in the
+        // wavefront (a wave-uniform test), each scale is its code shifted into the float32
+        // exponent field, two instructions instead of six
+        bool normal = false;
+        if constexpr (FMT == FMT_MXFP4) {
+            uint32_t sp = 0;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) sp |= e8m0_special_bytes(sq[j][0]);
+            normal = __builtin_amdgcn_ballot_w64(sp != 0) == 0;
+        }
+        auto ksteps = [&](auto normalc) {
+        constexpr bool NORMAL = decltype(normalc)::value;
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
             const bf16x8 af = *reinterpret_cast<const bf16x8 *>(base + xfrag[t]);
@@ -255,8 +267,10 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                 u32x4 bw;
                 if (FMT == FMT_INT4) bw = dec_int4(wq[j][t]);
                 else if (FMT == FMT_INT8) bw = dec_int8<false>(wq[j][2 * t], wq[j][2 * t + 1]);
-                else if (FMT == FMT_MXFP4) bw = dec_mxfp4(wq[j][t], e8m0_to_f32((sq[j][0] >> (8 * t)) & 0xFFu));
-                else {
+                else if (FMT == FMT_MXFP4) {
+                    const uint32_t e = (sq[j][0] >> (8 * t)) & 0xFFu;
+                    bw = dec_mxfp4(wq[j][t], NORMAL ? e8m0_to_f32_normal(e) : e8m0_to_f32(e));
+                } else {
                     bw = dec_cb4(wq[j][t], lut);
                     if constexpr (SPLIT) {
                         // the residual term first, then the leading term
@@ -296,6 +310,9 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
                 }
             }
         }
+        };
+        if (FMT == FMT_MXFP4 && normal) ksteps(std::true_type{});
+        else ksteps(std::false_type{});
     };
 
 #pragma unroll

@@ -189,6 +189,35 @@ def test_mxfp4_extreme_scales_dequant_exact():
     assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
 
 
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("tile", [None, 0, 20, 23])
+def test_mxfp4_special_scales_forward(M, tile):
+    """The decode kernel converts a chunk's E8M0 scales by shifting the code into the
+    float32 exponent field when no code of the chunk is 0 or 255 anywhere in the
+    wavefront, and exactly otherwise.  Codes 0 and 255 planted in a few blocks take the
+    exact path in their chunks while the others take the short one, in one launch: the
+    output matches the oracle, NaN (code 255) in exactly the oracle's columns."""
+    Q = _lib()
+    N, K = 112, 1024                  # seven column tiles, eight 128-input chunks
+    rng = np.random.default_rng(31)
+    q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    e = rng.integers(118, 125, size=(N, K // 32)).astype(np.uint8)
+    e[5, 3] = 0                       # 2^-127: a subnormal scale
+    e[40, 17] = 255                   # NaN: column 40 of every row
+    e[100, 30] = 0
+    canon = dict(codes=O.pack_nibbles(q), scales=e, group=32)
+    codes, scales, _ = to_device("mxfp4", canon)
+    pw = Q.pack("mxfp4", N, K, 32, codes, scales)
+    x = S.to_bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    yref = O.forward("mxfp4", x, canon, K, None)
+    sched = None if tile is None else (tile, 1)
+    y32 = Q.linear(bf16_tensor(x), pw, None, out_dtype=torch.float32, schedule=sched).cpu().numpy()
+    nan = np.isnan(yref)
+    assert nan[:, 40].all() and nan.sum() == M
+    assert np.array_equal(np.isnan(y32), nan)
+    assert rel_err(y32[~nan], yref[~nan]) <= TOL
+
+
 FWD_CASES = [c for c in CASES]
 
 
