@@ -173,19 +173,21 @@ __host__ __device__ constexpr int gemv_zero_blocks(int fmt, bool zp, int gs, int
 }
 // activation rows of one 1 KiB load: 64 16-byte pieces, chunk_k(fmt) / 8 pieces a row
 __host__ __device__ constexpr int gemv_rows_per_load(int fmt) { return 64 / (chunk_k(fmt) / 8); }
-__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt, bool sw = false) {
+__host__ __device__ constexpr int gemv_stage_bytes(int fmt, bool zp, int gs, int nt, bool sw = false, bool x1 = false) {
     return nt * TILE_BYTES + 256 * (gemv_scale_blocks(fmt, gs, nt) + gemv_zero_blocks(fmt, zp, gs, nt)) +
-           (sw ? 2048 : 16 * chunk_k(fmt) * 2);
+           (sw ? 2048 : (x1 ? 1024 : 16 * chunk_k(fmt) * 2));
 }
 constexpr int LDS_BYTES_MAX = 160 * 1024;
 // ring depth: PF stages per wavefront, fewer if they would not fit the LDS
-__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
-    return pf * wk * gemv_stage_bytes(fmt, zp, gs, nt, sw) <= LDS_BYTES_MAX
+__host__ __device__ constexpr int gemv_ring_depth(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false,
+                                                 bool x1 = false) {
+    return pf * wk * gemv_stage_bytes(fmt, zp, gs, nt, sw, x1) <= LDS_BYTES_MAX
                ? pf
-               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt, sw));
+               : LDS_BYTES_MAX / (wk * gemv_stage_bytes(fmt, zp, gs, nt, sw, x1));
 }
-__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false) {
-    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf, sw) * gemv_stage_bytes(fmt, zp, gs, nt, sw);
+__host__ __device__ constexpr int gemv_lds_bytes(int fmt, bool zp, int gs, int nt, int wk, int pf, bool sw = false,
+                                                bool x1 = false) {
+    return wk * gemv_ring_depth(fmt, zp, gs, nt, wk, pf, sw, x1) * gemv_stage_bytes(fmt, zp, gs, nt, sw, x1);
 }
 // k-parts a ring schedule runs with for a format: its WK where the chunk's k-steps
 // divide evenly, else 2
@@ -216,6 +218,7 @@ struct Plan {
     int cfg = 0;          // index into TILE_CFGS
     int mtiles = 1, nblocks = 1, ks = 1, cps = 1;
     bool fuse_swiglu = false;   // the decode kernel forms h from the raw input itself
+    bool x1 = false;            // decode: the rows fit one activation load per chunk
     size_t ws_h = 0;            // bytes of the materialised SwiGLU input at offset 0
     size_t ws_bytes = 0;        // ws_h + split-K partial sums
 };
@@ -255,7 +258,12 @@ inline bool is_decode(int cfg) { return TILE_CFGS[cfg].kind == 0; }
 // (measured at 4096 x 14336: 8.9 against 9.3 us at M = 1; at M = 16, with four
 // activation loads per chunk, and at 4096 x 4096, four chunks per wavefront, two-deep
 // is as fast or faster).
-inline int decode_cfg(int64_t ntiles, int64_t kchunks, int64_t M) {
+// When the rows fit one activation load (the one-load stage: 36 KiB of LDS for the
+// single-tile schedule, four workgroups per CU) and there are at least four column tiles
+// per CU, one tile per workgroup streams best (measured at 28672 x 4096 MXFP4: 13.15
+// against 14.72 us at M = 1; at 8192 x 28672, two tiles per CU, two-tile workgroups stay
+// ahead).
+inline int decode_cfg(int64_t ntiles, int64_t kchunks, int64_t M, int64_t rows_per_load) {
     constexpr int cands[] = {0, 1, 19, 2, 20};
     int best = 0;
     int64_t best_load = -1;
@@ -267,13 +275,14 @@ inline int decode_cfg(int64_t ntiles, int64_t kchunks, int64_t M) {
             best_load = load;
         }
     }
+    if (M <= rows_per_load && ntiles >= 4 * 256) best = 0;
     if (best == 0 && M <= 4 && ceil_div(kchunks, int64_t(TILE_CFGS[0].WK)) >= 12) best = 23;
     return best;
 }
 
 inline int default_cfg(const Layout &L, int64_t M) {
     const bool intf = L.fmt == FMT_INT4 || L.fmt == FMT_INT8;
-    if (M <= 16) return decode_cfg(L.ntiles, L.kchunks, M);
+    if (M <= 16) return decode_cfg(L.ntiles, L.kchunks, M, gemv_rows_per_load(L.fmt));
     if (M <= 32) return intf ? 17 : 5;
     if (M <= 64) return 7;
     const bool streamed = L.w_bytes >= (size_t(16) << 20);
@@ -308,6 +317,7 @@ inline Plan make_plan(const Layout &L, int64_t M, int cfg, int splits, int num_c
         p.cps = int(cpw);
         p.ks = 1;
         p.fuse_swiglu = swiglu && M <= SWIGLU_FUSE_MAX_M;
+        p.x1 = !p.fuse_swiglu && M <= gemv_rows_per_load(L.fmt);
         if (swiglu && !p.fuse_swiglu) p.ws_h = round256(size_t(M) * size_t(L.K) * 2);
         p.ws_bytes = p.ws_h;
         return p;

@@ -21,17 +21,18 @@ template <int FMT, bool ZP, int GS, int I>
 hipError_t launch_one(const Plan &p, const GemmArgs &a, hipStream_t st) {
     constexpr TileCfg t = TILE_CFGS[I];
     if constexpr (t.kind == 0) {
-        auto go = [&](auto sw) {
-            constexpr bool SW = decltype(sw)::value;
-            auto kern = qgemv_kernel<FMT, ZP, GS, t.NT, t.WK, t.PF, SW>;
-            constexpr size_t lds = gemv_lds_bytes(FMT, ZP, GS, t.NT, t.WK, t.PF, SW);
+        auto go = [&](auto sw, auto x1) {
+            constexpr bool SW = decltype(sw)::value, X1 = decltype(x1)::value;
+            auto kern = qgemv_kernel<FMT, ZP, GS, t.NT, t.WK, t.PF, SW, X1>;
+            constexpr size_t lds = gemv_lds_bytes(FMT, ZP, GS, t.NT, t.WK, t.PF, SW, X1);
             static bool attr_set = false;
             hipError_t e = allow_dynamic_lds((const void *)kern, lds, attr_set);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL(kern, dim3(p.nblocks, a.tile_map ? a.slots : 1), dim3(64 * t.WK), lds, st, a);
             return hipSuccess;
         };
-        hipError_t e = p.fuse_swiglu ? go(std::true_type{}) : go(std::false_type{});
+        hipError_t e = p.fuse_swiglu ? go(std::true_type{}, std::false_type{})
+                       : (p.x1 ? go(std::false_type{}, std::true_type{}) : go(std::false_type{}, std::false_type{}));
         if (e != hipSuccess) return e;
     } else {
         static_assert(t.kind == 2, "decode or LDS-ring schedule");

@@ -6,7 +6,8 @@
 // private LDS ring, as many chunks ahead as the schedule's ring depth (two, or four for
 // one column tile over a long input dimension), with direct buffer->LDS loads only: per chunk
 // the packed weight tiles, the scale and zero-point words and the activation block
-// (16 rows x one chunk of inputs).  The activation loads read whole rows of the chunk
+// (16 rows x one chunk of inputs; one load of rows, X1, when the batch fits it, which
+// shrinks the stage so that more workgroups share a CU).  The activation loads read whole rows of the chunk
 // (full 128-byte lines) and only the rows below M are requested; a XOR swizzle of the
 // 16-byte pieces makes each A-fragment read a conflict-free ds_read_b128.  Nothing is
 // loaded into registers, so every wait is explicit: a wavefront waits (vmcnt) only for
@@ -39,7 +40,7 @@
 
 namespace ql {
 
-template <int FMT, bool ZP, int GS, int NT, int WK, int PF, bool SW>
+template <int FMT, bool ZP, int GS, int NT, int WK, int PF, bool SW, bool X1>
 __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int CH = chunk_k(FMT);
     constexpr int STEPS = CH / 32;
@@ -51,10 +52,11 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     constexpr int S_OFF = NT * TILE_BYTES;
     constexpr int Z_OFF = S_OFF + 256 * NSS;
     constexpr int X_OFF = Z_OFF + 256 * NSZ;
-    constexpr int NI = SW ? 1 : XB::NI;               // activation loads a stage holds
+    constexpr int NI = (SW || X1) ? 1 : XB::NI;      // activation loads a stage holds
     constexpr int G_OFF = X_OFF + NI * 1024;          // gate rows (SW)
-    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT, SW);
-    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF, SW);
+    constexpr int STAGE = gemv_stage_bytes(FMT, ZP, GS, NT, SW, X1);
+    constexpr int S = gemv_ring_depth(FMT, ZP, GS, NT, WK, PF, SW, X1);
+    static_assert(!(SW && X1), "one activation layout");
     static_assert(G_OFF + (SW ? 1024 : 0) == STAGE && S >= 1 && S <= 8, "stage layout");
     static_assert(gemv_rows_per_load(FMT) == XB::RPI, "rows per activation load");
     // fused SwiGLU: the batch's rows fit the first activation load; each lane forms HE
@@ -121,7 +123,7 @@ __global__ void __launch_bounds__(64 * WK) qgemv_kernel(GemmArgs a) {
     uint32_t xfrag[STEPS];
 #pragma unroll
     for (int t = 0; t < STEPS; ++t)
-        xfrag[t] = uint32_t(X_OFF + XB::slot(SW ? c % XB::RPI : c, 4 * t + g));
+        xfrag[t] = uint32_t(X_OFF + XB::slot((SW || X1) ? c % XB::RPI : c, 4 * t + g));
     // scale / zero-point words: word e of a chunk's scale block is word (e % 8) of the
     // record of tile e / (8 SPC), group slot (e / 8) % SPC (MXFP4: column e % 16 of tile
     // e / 16); zero-point words likewise with 2 words per record

@@ -227,9 +227,11 @@ def test_schedule_entry_points(L):
 
 def test_decode_schedule_choice(L):
     """Decode schedules (M <= 16): the column tiles per workgroup follow the busiest
-    compute unit's load (256 CUs), and a single-tile workgroup over a long input
-    dimension (eight wavefronts of 12 chunks or more) at up to 4 rows takes the
-    four-deep ring instead of the two-deep one (same tile shape, another schedule)."""
+    compute unit's load (256 CUs); where the rows fit one activation load and there are
+    four column tiles or more per CU, one tile per workgroup; and a single-tile workgroup
+    over a long input dimension (eight wavefronts of 12 chunks or more) at up to 4 rows
+    takes the four-deep ring instead of the two-deep one (same tile shape, another
+    schedule)."""
     import bit_weight_only_offline_amd as Q
     r, c, k = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
 
@@ -247,8 +249,11 @@ def test_decode_schedule_choice(L):
     d1, d4, d16 = (pick(MXFP4, M, 4096, 14336, 32) for M in (1, 4, 16))
     assert d1 == d4 and d1[1] == d16[1] == (16, 16) and d1[0] != d16[0]
     assert d16[0] == t4[16][0]
-    # 28672 x 4096 MXFP4 gate/up: 1792 column tiles -> seven per workgroup (256 workgroups)
-    assert pick(MXFP4, 1, 28672, 4096, 32)[1] == (16, 112)
+    # 28672 x 4096 MXFP4 gate/up: 1792 column tiles -> seven per workgroup (256 workgroups),
+    # but one per workgroup where the rows fit one activation load (four workgroups per CU)
+    assert pick(MXFP4, 16, 28672, 4096, 32)[1] == (16, 112)
+    assert pick(MXFP4, 1, 28672, 4096, 32)[1] == pick(MXFP4, 4, 28672, 4096, 32)[1] == (16, 16)
+    assert pick(MXFP4, 5, 28672, 4096, 32)[1] == (16, 112)
     # 8192 x 28672 INT8 with the SwiGLU input: 512 column tiles -> two per workgroup
     assert pick(INT8, 1, 8192, 28672, 256, 1)[1] == (16, 32)
 
