@@ -222,7 +222,7 @@ FWD_CASES = [c for c in CASES]
 
 
 @pytest.mark.parametrize("case", FWD_CASES, ids=[c[0] for c in FWD_CASES])
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 40, 64, 65, 150])
+@pytest.mark.parametrize("M", [1, 4, 5, 8, 9, 16, 17, 40, 64, 65, 150])   # 4 / 8: the most rows one activation load holds
 def test_forward_parity(case, M):
     Q = _lib()
     name, fmt, G, sym, N, K = case
